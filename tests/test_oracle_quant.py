@@ -1,0 +1,158 @@
+"""Pins for the oracle's quantizers (CPU only).
+
+Independent of the oracle: exact Fraction arithmetic for fl32(amax/448) and
+fl32(x/s), nearest-code search over torch's E4M3 values, closed forms for
+special tiles, and the error bound that RNE to 3 mantissa bits implies.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_block_scaled_04_amd import synth
+from oracle import bf16, e4m3, quantize
+from tests._exact import e4m3_table, nearest_code, rn32, tile_scale_exact
+
+TAB = e4m3_table()
+
+
+def tdec(q):
+    return torch.from_numpy(np.ascontiguousarray(q, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def check_tile_invariants(x32, q, s_rows, pow2):
+    """x32[R][C] float32 input, q[R][C], s_rows[R][C/128]."""
+    R, C = x32.shape
+    deq = tdec(q)
+    assert not np.isnan(deq).any()
+    for r in range(R):
+        for t in range(C // 128):
+            xs = x32[r, t * 128:(t + 1) * 128].astype(np.float64)
+            qs = deq[r, t * 128:(t + 1) * 128]
+            s = float(s_rows[r, t])
+            amax = np.max(np.abs(xs))
+            if amax == 0:
+                assert s == 1.0 and np.all(qs == 0)
+                continue
+            if pow2:
+                assert np.frexp(s)[0] == 0.5                   # a power of two
+                assert 224.0 <= np.max(np.abs(qs)) <= 448.0
+            else:
+                at = np.abs(xs) == amax
+                assert np.all(np.abs(qs[at]) == 448.0)
+            y = np.abs(xs) / s
+            err = np.abs(qs * s - xs)
+            normal = y >= 2.0 ** -6
+            assert np.all(err[normal] <= (2.0 ** -4 + 2.0 ** -22) * np.abs(xs[normal]))
+            assert np.all(err[~normal] <= (2.0 ** -10 + 2.0 ** -22) * s)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_quantize_1x128_invariants_on_workload_recipe(pow2):
+    x = synth.activation(64, 1024, seed=5)["a"]
+    q, s = quantize.quantize_1x128(x, pow2)
+    assert q.shape == (64, 1024) and s.shape == (8, 64) and s.dtype == np.float32
+    check_tile_invariants(bf16.to_f32(x), q, s.T, pow2)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_quantize_1x128_brute_force_exact(pow2):
+    rng = np.random.default_rng(7)
+    x32 = (rng.standard_normal((3, 256)) * 2.0 ** rng.integers(-30, 30, (3, 1))).astype(np.float32)
+    x32[1, 130] *= 1000                                       # an outlier in one tile
+    xb = synth.bf16_bits(x32)
+    xf = bf16.to_f32(xb)
+    q, s = quantize.quantize_1x128(xb, pow2)
+    for r in range(3):
+        for t in range(2):
+            tile = xf[r, t * 128:(t + 1) * 128].astype(np.float64)
+            st = tile_scale_exact(float(np.max(np.abs(tile))), pow2)
+            assert float(s[t, r]) == st
+            for c in range(128):
+                y = rn32(Fraction(float(tile[c])) / Fraction(st))
+                assert q[r, t * 128 + c] == nearest_code(y, TAB), (r, t, c)
+
+
+def test_quantize_special_tiles():
+    x = np.zeros((4, 256), np.float32)
+    x[0, :128] = 3.0                      # constant tile
+    x[1, :128] = -0.0078125               # negative constant tile
+    x[2, 5] = 1e-30                       # single tiny nonzero (BF16 rounds it)
+    x[3, 128:] = 7.0
+    xb = synth.bf16_bits(x)
+    q, s = quantize.quantize_1x128(xb)
+    assert np.all(q[0, :128] == 0x7E) and s[0, 0] == np.float32(rn32(Fraction(3) / 448))
+    assert np.all(q[1, :128] == 0xFE)
+    assert q[2, 5] == 0x7E and np.all(np.delete(q[2, :128], 5) == 0)
+    assert np.all(q[0, 128:] == 0) and s[1, 0] == 1.0                # zero tile
+    assert np.all(q[3, 128:] == 0x7E) and s[0, 3] == 1.0
+    # negative zeros keep their sign
+    z = synth.bf16_bits(np.full((1, 128), -0.0, np.float32))
+    qz, sz = quantize.quantize_1x128(z)
+    assert np.all(qz == 0x80) and sz[0, 0] == 1.0
+
+
+def test_quantize_values_cannot_overflow():
+    # amax / fl32(amax/448) stays below the rounding boundary 464 for every BF16 amax
+    bits = np.arange(0x0001, 0x7F80, dtype=np.uint16)         # all positive finite BF16
+    amax = bf16.to_f32(bits)
+    s = quantize.tile_scale(amax, False)
+    y = np.divide(amax, s, dtype=np.float32)
+    # 0x7E's rounding interval is (432, 464); a normal scale keeps y within
+    # 2^-22 of 448, a subnormal one (amax < 448 * 2^-126) only within ~0.3%.
+    assert np.all(y < 464.0) and np.all(y > 432.0)
+    normal = s >= np.float32(2.0 ** -126)
+    assert np.all(np.abs(y[normal] - 448.0) <= 448.0 * 2.0 ** -22)
+    assert np.all(e4m3.encode(y) == 0x7E)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_transpose_requant_invariants_and_brute_force(pow2):
+    x = synth.activation(256, 256, seed=9)["a"]
+    q, s = quantize.quantize_1x128(x)
+    qt, st = quantize.quantize_transpose_128x1(q, s, pow2)
+    assert qt.shape == (256, 256) and st.shape == (2, 256)
+    # d = fl32(dec(q) * s_row), exactly
+    d = np.empty((256, 256), np.float64)
+    deq = tdec(q)
+    for m in range(256):
+        for kb in range(2):
+            for k in range(kb * 128, kb * 128 + 128):
+                d[m, k] = rn32(Fraction(float(deq[m, k])) * Fraction(float(s[kb, m])))
+    dT = d.T.astype(np.float32)
+    check_tile_invariants(dT, qt, st.T, pow2)
+    # brute force on a few columns of the transposed output
+    for k in (0, 1, 77, 128, 255):
+        for mb in range(2):
+            col = d[mb * 128:(mb + 1) * 128, k]
+            sc = tile_scale_exact(float(np.max(np.abs(col))), pow2)
+            assert float(st[mb, k]) == sc
+            for i in range(0, 128, 7):
+                y = rn32(Fraction(float(col[i])) / Fraction(sc))
+                assert qt[k, mb * 128 + i] == nearest_code(y, TAB)
+
+
+@pytest.mark.parametrize("N", [256, 200, 64])
+def test_quantize_128x128_blocks(N):
+    w = synth.dense(8, N, 384, seed=11)["b"]
+    q, s = quantize.quantize_128x128(w)
+    nb = -(-N // 128)
+    assert q.shape == (N, 384) and s.shape == (nb, 3)
+    xf = bf16.to_f32(w).astype(np.float64)
+    deq = tdec(q)
+    for i in range(nb):
+        for j in range(3):
+            blk = xf[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            qb = deq[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            sc = tile_scale_exact(float(np.max(np.abs(blk))), False)
+            assert float(s[i, j]) == sc
+            assert np.all(np.abs(qb[np.abs(blk) == np.max(np.abs(blk))]) == 448.0)
+            err = np.abs(qb * sc - blk)
+            nrm = np.abs(blk) / sc >= 2.0 ** -6
+            assert np.all(err[nrm] <= (2.0 ** -4 + 2.0 ** -22) * np.abs(blk[nrm]))
+    # grouped weights quantize expert by expert
+    wg = np.stack([w, w[::-1]])
+    qg, sg = quantize.quantize_128x128(wg)
+    assert np.array_equal(qg[0], q) and sg.shape == (2, nb, 3)
