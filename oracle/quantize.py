@@ -23,7 +23,9 @@ What they compute, and where it comes from:
 Per tile (readings where the pages are silent):
   amax = max |x| over the tile (exact);
   s    = 1.0                         if amax == 0,
-         fl32(amax / 448)            otherwise (correctly rounded FP32 divide);
+         fl32(amax / 448)            otherwise (correctly rounded FP32 divide;
+                                     clamped below at 2^-149 so a nonzero
+                                     tile never gets a zero scale);
   s    = 2^ceil(log2 s)              with the power-of-two option;
   q    = enc(fl32(x / s))            RNE to E4M3 with satfinite, after an FP32
                                      divide (not a multiply by a reciprocal).
@@ -48,6 +50,10 @@ def tile_scale(amax_f32, pow2: bool) -> np.ndarray:
     amax = np.asarray(amax_f32, dtype=np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         s = np.divide(amax, _448, dtype=np.float32)
+    # A nonzero tile never gets a zero scale: when amax/448 underflows FP32
+    # (amax < 2^-140, unreachable from BF16 inputs) the smallest positive
+    # FP32, 2^-149, is used instead.
+    s = np.maximum(s, np.float32(2.0 ** -149))
     s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
     if pow2:
         f, e = np.frexp(s.astype(np.float64))          # s = f * 2^e, f in [0.5, 1)

@@ -57,10 +57,11 @@ def nearest_code(y: float, table=None) -> int:
 
 def tile_scale_exact(amax: float, pow2: bool) -> float:
     """Scale of a tile from exact arithmetic: nearest float32 to amax/448
-    (1 for a zero tile), rounded up to a power of two on request."""
+    (1 for a zero tile, at least 2^-149 for a nonzero one), rounded up to a
+    power of two on request."""
     if amax == 0:
         return 1.0
-    s = rn32(Fraction(amax) / 448)
+    s = max(rn32(Fraction(amax) / 448), 2.0 ** -149)
     if pow2:
         e = ilog2(Fraction(s))
         if Fraction(2) ** e != Fraction(s):

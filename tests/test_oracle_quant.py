@@ -156,3 +156,13 @@ def test_quantize_128x128_blocks(N):
     wg = np.stack([w, w[::-1]])
     qg, sg = quantize.quantize_128x128(wg)
     assert np.array_equal(qg[0], q) and sg.shape == (2, nb, 3)
+
+
+def test_underflowing_scale_is_clamped_to_smallest_float32():
+    # float32 tiles (the transpose path) can be small enough that amax/448
+    # underflows; their scale is 2^-149 and codes are enc(fl32(x / 2^-149)).
+    x = np.zeros((1, 128), np.float32)
+    x[0, :4] = [2.0 ** -145, -(2.0 ** -147), 2.0 ** -149, 0.0]
+    q, s = quantize.quantize_rows_f32(x)
+    assert s[0, 0] == np.float32(2.0 ** -149) == np.float32(tile_scale_exact(2.0 ** -145, False))
+    assert q[0, :4].tolist() == [nearest_code(16.0, TAB), nearest_code(-4.0, TAB), nearest_code(1.0, TAB), 0]
