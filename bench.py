@@ -1,0 +1,234 @@
+"""Benchmark of the block-scaled FP8 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+
+One step = one pass of the forward hot path of an FP8 linear layer on the
+4096 x 2112 x 7168 training-shaped projection: 1x128 quantization of the BF16
+activation [4096][7168] followed by the block-scaled FP8 GEMM against the
+128x128-quantized weight [2112][7168] (weights are quantized once, before
+timing, as a training step would for a resident weight).  `value` is GEMM
+TFLOP/s over the whole step (2*M*N*K / step time); inputs are resident in HBM
+before the timed region.
+
+Printed as one JSON line, with
+  roofline      the GEMM kernel alone, timed with HIP events on the stream it
+                runs on, against the MI355X dense FP8 MFMA peak (5.0 PFLOP/s);
+  cpu_baseline  the CPU oracle (NumPy, float64) timed on this host on a
+                256-row slice of the same workload;
+  kernels       every kernel of the hot path on its own workload (1x128 and
+                transpose quantizers on 8192 x 7168, the decode-shaped GEMM
+                128 x 24576 x 1536 with its quantizer, the MoE contiguous and
+                masked grouped GEMMs), HBM-bound ones over rotating buffers so
+                the 256 MB last-level cache does not serve repeats.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+WORKLOAD = dict(name="dense_4096x2112x7168", M=4096, N=2112, K=7168)
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def time_events(fn, iters, warmup=3):
+    """Average device time of fn() in microseconds, from HIP events recorded on
+    torch's current stream (the stream the library launches on)."""
+    for _ in range(warmup):
+        fn()
+    start = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    end = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        start[i].record()
+        fn()
+        end[i].record()
+    torch.cuda.synchronize()
+    return float(np.mean([s.elapsed_time(e) for s, e in zip(start, end)])) * 1e3
+
+
+def rotation(bytes_per_set, min_total=1 << 29):
+    return int(max(1, -(-min_total // max(bytes_per_set, 1))))
+
+
+def extra_kernels(fb, synth):
+    """Per-kernel measurements on each workload of the hot path."""
+    out = {}
+    # 1x128 quantizer and transpose-requant on the 8192 x 7168 activation
+    M, K = 8192, 7168
+    x_bits = synth.activation(M, K, seed=0)["a"]
+    x0 = dev_bf16(x_bits)
+    R = rotation(3 * M * K)
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    qs = [fb.quantize_1x128(x) for x in xs]
+    it = iter(range(10 ** 9))
+    us = time_events(lambda: fb.quantize_1x128(xs[next(it) % R]), 30)
+    byt = 2 * M * K + M * K + 4 * M * (K // 128)
+    out["quantize_1x128_8192x7168"] = dict(us=us, GBs=byt / us / 1e3, frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS,
+                                           bytes=byt)
+    it = iter(range(10 ** 9))
+    us = time_events(lambda: fb.quantize_transpose_128x1(*qs[next(it) % R]), 30)
+    byt = 2 * M * K + 4 * (M * K // 128) * 2
+    out["quantize_transpose_128x1_8192x7168"] = dict(us=us, GBs=byt / us / 1e3,
+                                                     frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
+    del xs, qs, x0
+    torch.cuda.empty_cache()
+
+    # decode-shaped GEMM 128 x 24576 x 1536 (power-of-two scales) + its quantizer
+    M, N, K = 128, 24576, 1536
+    w = synth.dense(M, N, K, seed=0)
+    xa = dev_bf16(w["a"])
+    wb = dev_bf16(w["b"])
+    a, sa = fb.quantize_1x128(xa, pow2=True)
+    R = rotation(N * K)
+    bsets = [fb.quantize_128x128(wb, pow2=True) for _ in range(R)]
+    it = iter(range(10 ** 9))
+    us = time_events(lambda: fb.gemm(a, sa, *bsets[next(it) % R]), 30)
+    byt = M * K + N * K + 2 * M * N + 4 * (M * K // 128) + 4 * (N // 128) * (K // 128)
+    out["gemm_decode_128x24576x1536_pow2"] = dict(us=us, TFLOPs=2 * M * N * K / us / 1e6,
+                                                  GBs=byt / us / 1e3, frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS,
+                                                  bytes=byt)
+    us = time_events(lambda: fb.quantize_1x128(xa, pow2=True), 30)
+    out["quantize_1x128_128x1536_pow2"] = dict(us=us, GBs=(3 * M * K + 4 * M * K // 128) / us / 1e3)
+    del bsets, wb
+    torch.cuda.empty_cache()
+
+    # MoE contiguous 8 x (sum M = 8192) x 4096 x 7168
+    G, Mt, N, K = 8, 8192, 4096, 7168
+    w = synth.contiguous(G, Mt, N, K, seed=0)
+    a, sa = fb.quantize_1x128(dev_bf16(w["a"]))
+    b, sb = fb.quantize_128x128(dev_bf16(w["b"]))
+    offs = torch.from_numpy(w["m_offsets"]).cuda()
+    us = time_events(lambda: fb.grouped_gemm_contiguous(a, sa, b, sb, offs), 20)
+    out["grouped_contiguous_8x8192x4096x7168"] = dict(us=us, TFLOPs=2 * Mt * N * K / us / 1e6,
+                                                      frac_mfma=2 * Mt * N * K / us / 1e6 / FP8_PEAK_TFLOPS)
+    del a, sa, b, sb
+    torch.cuda.empty_cache()
+
+    # MoE masked 32 x 256 x 7168 x 2048 (decode)
+    G, cap, N, K = 32, 256, 7168, 2048
+    w = synth.masked(G, cap, N, K, seed=0)
+    a2, sa2 = fb.quantize_1x128(dev_bf16(w["a"].reshape(G * cap, K)))
+    a = a2.view(G, cap, K)
+    sa = sa2.view(K // 128, G, cap).permute(1, 0, 2).contiguous()
+    wbits = dev_bf16(w["b"])
+    b, sb = fb.quantize_128x128(wbits)
+    del wbits
+    cnt = torch.from_numpy(w["masked_m"]).cuda()
+    c = w["masked_m"].astype(np.int64)
+    flops = 2 * int(c.sum()) * N * K
+    nz = int((c > 0).sum())
+    byt = nz * (N * K + 4 * (N // 128) * (K // 128)) + int(c.sum()) * (K + 4 * K // 128 + 2 * N)
+    us = time_events(lambda: fb.grouped_gemm_masked(a, sa, b, sb, cnt), 20)
+    out["grouped_masked_32x256x7168x2048"] = dict(us=us, TFLOPs=flops / us / 1e6, GBs=byt / us / 1e3,
+                                                  frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
+    return out
+
+
+def cpu_baseline(synth):
+    """The CPU oracle on a 256-row slice of the workload (1x128 quantization of
+    the slice + its GEMM against the full weight), in TFLOP/s of GEMM work."""
+    from oracle import gemm as og, quantize as oq
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    M, N, K = 256, WORKLOAD["N"], WORKLOAD["K"]
+    w = synth.dense(WORKLOAD["M"], N, K, seed=0)
+    bq, bs = oq.quantize_128x128(w["b"])
+    t0 = time.perf_counter()
+    a, sa = oq.quantize_1x128(w["a"][:M])
+    _ = og.gemm_ref(a, sa, bq, bs, "bf16")
+    dt = time.perf_counter() - t0
+    return dict(value=2 * M * N * K / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"rows 0..255 of A (256x{K}) quantized 1x128 and multiplied by the full "
+                       f"{N}x{K} weight: {2 * M * N * K / 1e9:.2f} GFLOP in {dt:.2f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel workload table")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a single "
+              "device; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    from fp8_block_scaled_04_amd import fp8bs as fb, synth
+
+    M, N, K = WORKLOAD["M"], WORKLOAD["N"], WORKLOAD["K"]
+    w = synth.dense(M, N, K, seed=0)
+    x = dev_bf16(w["a"])
+    bq, bs = fb.quantize_128x128(dev_bf16(w["b"]))
+    d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    gemm_start, gemm_end = [], []
+
+    def step(record):
+        q, s = fb.quantize_1x128(x)
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fb.gemm(q, s, bq, bs, out=d)
+            e1.record()
+            gemm_start.append(e0)
+            gemm_end.append(e1)
+        else:
+            fb.gemm(q, s, bq, bs, out=d)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt / args.steps * 1e3
+    gemm_us = float(np.mean([a.elapsed_time(b) for a, b in zip(gemm_start, gemm_end)])) * 1e3
+    flops = 2.0 * M * N * K
+    achieved = flops / gemm_us / 1e6
+    rec = {
+        "metric": "FP8 block-scaled GEMM TFLOPS (% of MI355X FP8 peak); quantizer GB/s",
+        "value": flops / (ms_per_step / 1e3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": "fp8 linear forward: quantize_1x128(A bf16 4096x7168) + block-scaled GEMM "
+                               "4096x2112x7168, bf16 out", "M": M, "N": N, "K": K},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "k_gemm (dense)", "kernel_us": gemm_us},
+    }
+    if not args.no_extra:
+        rec["kernels"] = extra_kernels(fb, synth)
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

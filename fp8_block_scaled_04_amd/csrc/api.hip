@@ -1,0 +1,175 @@
+// C ABI of libfp8bs: argument checks, device check, dispatch to launchers.
+// The operations and their sources on the surveyed pages are documented in
+// include/fp8bs.h next to each declaration.
+#include <atomic>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "fp8bs.h"
+#include "launch.h"
+
+namespace {
+
+using fp8bs::GemmProblem;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The current device must be a gfx950 (MI355X / MI350X).  The answer is
+// cached per device ordinal; hipGetDevice itself fails when no GPU exists.
+fp8bs_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8BS_ERR_DEVICE;
+  if (dev >= kMaxDevices) return FP8BS_ERR_DEVICE;
+  int st = g_device_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8BS_ERR_DEVICE;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? FP8BS_OK : FP8BS_ERR_DEVICE;
+}
+
+fp8bs_status launched(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH; }
+
+constexpr int64_t kMaxGridY = 65535;
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8bs_status_str(fp8bs_status s) {
+  switch (s) {
+    case FP8BS_OK: return "ok";
+    case FP8BS_ERR_NULL: return "a required pointer is NULL";
+    case FP8BS_ERR_SHAPE: return "invalid size (negative, or breaks a divisibility rule)";
+    case FP8BS_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FP8BS_ERR_FLAGS: return "unknown flags or output dtype";
+    case FP8BS_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
+    case FP8BS_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t fp8bs_abi_version(void) { return FP8BS_ABI_VERSION; }
+
+fp8bs_status fp8bs_quantize_1x128(const void* x, int64_t M, int64_t K, uint8_t* q, float* s, uint32_t flags,
+                                  fp8bs_stream_t stream) {
+  if (M < 0 || K <= 0 || K % 128) return FP8BS_ERR_SHAPE;
+  if ((K / 128 + 3) / 4 > kMaxGridY) return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
+  if (M == 0) return FP8BS_OK;
+  if (!x || !q || !s) return FP8BS_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return FP8BS_ERR_ALIGN;
+  if (fp8bs_status st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_quantize_1x128(x, M, K, q, s, flags & FP8BS_SCALE_POW2, (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_quantize_transpose_128x1(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt,
+                                            float* st, uint32_t flags, fp8bs_stream_t stream) {
+  if (M < 0 || K < 0 || M % 128 || K % 128) return FP8BS_ERR_SHAPE;
+  if (K / 128 > kMaxGridY) return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
+  if (M == 0 || K == 0) return FP8BS_OK;
+  if (!q || !s || !qt || !st) return FP8BS_ERR_NULL;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(qt) || !aligned16(st)) return FP8BS_ERR_ALIGN;
+  if (fp8bs_status e = check_device()) return e;
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_quantize_t128x1(q, s, M, K, qt, st, flags & FP8BS_SCALE_POW2, (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t K, uint8_t* q, float* s,
+                                    uint32_t flags, fp8bs_stream_t stream) {
+  if (G < 0 || N < 0 || K <= 0 || K % 128) return FP8BS_ERR_SHAPE;
+  if (G > kMaxGridY || K / 128 > kMaxGridY) return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
+  if (G == 0 || N == 0) return FP8BS_OK;
+  if (!w || !q || !s) return FP8BS_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return FP8BS_ERR_ALIGN;
+  if (fp8bs_status e = check_device()) return e;
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_quantize_128x128(w, G, N, K, q, s, flags & FP8BS_SCALE_POW2, (hipStream_t)stream));
+}
+
+namespace {
+
+fp8bs_status gemm_common(int64_t N, int64_t K, int32_t out_dtype) {
+  if (N < 0 || N % 16 || K <= 0 || K % 128) return FP8BS_ERR_SHAPE;
+  if (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_FP32) return FP8BS_ERR_FLAGS;
+  return FP8BS_OK;
+}
+
+fp8bs_status gemm_pointers(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, void* d,
+                           const int32_t* groups, bool need_groups) {
+  if (!a || !sa || !b || !sb || !d || (need_groups && !groups)) return FP8BS_ERR_NULL;
+  if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb) || !aligned16(d) ||
+      (need_groups && (reinterpret_cast<uintptr_t>(groups) & 3u)))
+    return FP8BS_ERR_ALIGN;
+  return FP8BS_OK;
+}
+
+// Tile counts must fit the 32-bit workgroup index and in-kernel int math.
+bool grid_fits(int64_t rows, int64_t N, int64_t groups) {
+  const int64_t tiles = ((rows + 127) / 128) * ((N + 127) / 128) * groups;
+  return tiles < (int64_t(1) << 30);
+}
+
+}  // namespace
+
+fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, void* d,
+                                        int64_t M, int64_t N, int64_t K, int32_t out_dtype, fp8bs_stream_t stream) {
+  if (M < 0) return FP8BS_ERR_SHAPE;
+  if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
+  if (!grid_fits(M, N, 1)) return FP8BS_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, nullptr, false)) return e;
+  if (fp8bs_status e = check_device()) return e;
+  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, out_dtype == FP8BS_OUT_FP32, fp8bs::kDense};
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                               void* d, const int32_t* m_offsets, int32_t G, int64_t Mt, int64_t N,
+                                               int64_t K, int32_t out_dtype, fp8bs_stream_t stream) {
+  if (G < 0 || Mt < 0 || Mt % 128) return FP8BS_ERR_SHAPE;
+  if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
+  if (!grid_fits(Mt, N, 1)) return FP8BS_ERR_SHAPE;
+  if (G == 0 || Mt == 0 || N == 0) return FP8BS_OK;
+  if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, m_offsets, true)) return e;
+  if (fp8bs_status e = check_device()) return e;
+  GemmProblem p{a, sa, b, sb, d, m_offsets, Mt, N, K, G, out_dtype == FP8BS_OUT_FP32, fp8bs::kContiguous};
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                           void* d, const int32_t* masked_m, int32_t G, int64_t cap, int64_t N,
+                                           int64_t K, int32_t out_dtype, fp8bs_stream_t stream) {
+  if (G < 0 || cap < 0) return FP8BS_ERR_SHAPE;
+  if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
+  if (!grid_fits(cap, N, G)) return FP8BS_ERR_SHAPE;
+  if (G == 0 || cap == 0 || N == 0) return FP8BS_OK;
+  if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, masked_m, true)) return e;
+  if (fp8bs_status e = check_device()) return e;
+  GemmProblem p{a, sa, b, sb, d, masked_m, cap, N, K, G, out_dtype == FP8BS_OUT_FP32, fp8bs::kMasked};
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_cast_f32_to_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream_t stream) {
+  if (n < 0) return FP8BS_ERR_SHAPE;
+  if (n == 0) return FP8BS_OK;
+  if (!x || !q) return FP8BS_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q)) return FP8BS_ERR_ALIGN;
+  if (fp8bs_status e = check_device()) return e;
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_cast_e4m3(x, n, q, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Internal launchers (host side) of libfp8bs.  Arguments are already checked
+// by the C ABI layer; these only configure grids and enqueue kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+hipError_t launch_quantize_1x128(const void* x, int64_t M, int64_t K, uint8_t* q, float* s, bool pow2,
+                                 hipStream_t stream);
+hipError_t launch_quantize_t128x1(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt, float* st,
+                                  bool pow2, hipStream_t stream);
+hipError_t launch_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t K, uint8_t* q, float* s, bool pow2,
+                                   hipStream_t stream);
+hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream);
+
+enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+struct GemmProblem {
+  const uint8_t* a;       // E4M3 activations
+  const float* sa;        // 1x128 scales
+  const uint8_t* b;       // E4M3 weights ([G][N][K] for grouped)
+  const float* sb;        // 128x128 scales
+  void* d;                // output
+  const int32_t* groups;  // m_offsets [G+1] (contiguous) or masked_m [G] (masked); device
+  int64_t M;              // rows: dense M, contiguous Mt, masked cap
+  int64_t N, K;
+  int32_t G;              // number of groups (1 for dense)
+  bool out_f32;
+  GemmMode mode;
+};
+
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+
+}  // namespace fp8bs

@@ -1,0 +1,261 @@
+// Fine-grained FP8 quantizers for gfx950.
+//
+//   quantize_1x128            BF16 [M][K] -> E4M3 [M][K] + FP32 [K/128][M]
+//   quantize_transpose_128x1  E4M3 [M][K] + [K/128][M] -> E4M3 [K][M] + FP32 [M/128][K]
+//   quantize_128x128          BF16 [G][N][K] -> E4M3 + FP32 [G][ceil(N/128)][K/128]
+//   cast_f32_to_e4m3          FP32 [n] -> E4M3 [n]
+//
+// Method: page 1 (the uniondaocoop.com post on DeepSeek's FP8 training
+// framework), paragraphs on 1x128 activation tiles and on converting cached
+// FP8 activations to 128x1 tiles for the backward pass; page 2 ("A Deadly
+// Mistake Uncovered on Deepseek China Ai"), power-of-two scaling factors.
+// Per tile: amax, s = fl32(amax/448) (see tile_scale), q = E4M3(fl32(x/s)).
+//
+// All four kernels are bound by HBM bandwidth: 128-bit loads and stores, tile
+// amax by DPP row reductions, no LDS except for the transpose.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8bs {
+namespace {
+
+// ---------------------------------------------------------------------------
+// 1x128: one tile = 16 lanes (one DPP row) x 8 BF16 each (one 16-byte load).
+// A workgroup of 256 lanes covers 16 rows; each lane walks kTiles tiles of its
+// row so that kTiles loads are in flight before any arithmetic.  Scales of 16
+// consecutive rows are written together (s is [K/128][M], M contiguous).
+// ---------------------------------------------------------------------------
+constexpr int kQ1Tiles = 4;
+
+template <bool POW2, bool SCALED>
+__device__ __forceinline__ uint2 quantize8(uint4 v, const TileScale& t) {
+  float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = div_rn(SCALED ? x[i] * t.sx : x[i], t.ss, t.r);
+  return make_uint2(pack4_e4m3(y[0], y[1], y[2], y[3]), pack4_e4m3(y[4], y[5], y[6], y[7]));
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void k_quantize_1x128(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                         uint8_t* __restrict__ q, float* __restrict__ s) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t m = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t KT = K / 128;
+  const int64_t kb0 = (int64_t)blockIdx.y * kQ1Tiles;
+  const bool row_ok = m < M;
+
+  uint4 v[kQ1Tiles];
+#pragma unroll
+  for (int t = 0; t < kQ1Tiles; ++t) {
+    const int64_t kb = kb0 + t;
+    v[t] = make_uint4(0, 0, 0, 0);
+    if (row_ok && kb < KT)
+      v[t] = *reinterpret_cast<const uint4*>(x + m * K + kb * 128 + lane16 * 8);
+  }
+#pragma unroll
+  for (int t = 0; t < kQ1Tiles; ++t) {
+    const int64_t kb = kb0 + t;
+    const uint4 w = v[t];
+    float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16_lo(w.x)), __builtin_fabsf(bf16_hi(w.x))),
+                              __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.y)), __builtin_fabsf(bf16_hi(w.y))));
+    float b = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16_lo(w.z)), __builtin_fabsf(bf16_hi(w.z))),
+                              __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.w)), __builtin_fabsf(bf16_hi(w.w))));
+    const float amax = row16_max(__builtin_fmaxf(a, b));
+    const TileScale ts = tile_scale<POW2>(amax);
+    uint2 out;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(ts.sx != 1.0f) != 0, 0))
+      out = quantize8<POW2, true>(w, ts);
+    else
+      out = quantize8<POW2, false>(w, ts);
+    if (row_ok && kb < KT) {
+      *reinterpret_cast<uint2*>(q + m * K + kb * 128 + lane16 * 8) = out;
+      if (lane16 == 0) s[kb * M + m] = ts.s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 -> 128x1 transpose-requantize.  One workgroup per 128x128 tile
+// (rows mb, columns kb).  Phase 1 stages the tile's 16 KB of codes and its
+// 128 row scales in LDS with 128-bit loads.  Phase 2 gives each lane half a
+// column (64 rows): dequantize d = fl32(dec(q) * s_row), take the column amax
+// with the partner lane, requantize and write 64 contiguous bytes of the
+// transposed row.  Adjacent lanes read adjacent bytes of one LDS row, so the
+// column walk has no bank conflicts.
+// ---------------------------------------------------------------------------
+template <bool POW2>
+__global__ __launch_bounds__(256) void k_quantize_t128x1(const uint8_t* __restrict__ q, const float* __restrict__ s,
+                                                          int64_t M, int64_t K,
+                                                          uint8_t* __restrict__ qt, float* __restrict__ st) {
+  __shared__ __attribute__((aligned(16))) uint8_t codes[128 * 128];
+  __shared__ __attribute__((aligned(16))) float rs[128];
+  const int64_t mb = blockIdx.x, kb = blockIdx.y;
+  const int t = threadIdx.x;
+  {
+    const int r = t >> 1, h = t & 1;
+    const uint4* src = reinterpret_cast<const uint4*>(q + (mb * 128 + r) * K + kb * 128 + h * 64);
+    uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+    uint4* dst = reinterpret_cast<uint4*>(codes + r * 128 + h * 64);
+    dst[0] = v0; dst[1] = v1; dst[2] = v2; dst[3] = v3;
+    if (t < 128) rs[t] = s[kb * M + mb * 128 + t];
+  }
+  __syncthreads();
+  const int c = t >> 1, h = t & 1;
+  float d[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const int r = h * 64 + i;
+    d[i] = __builtin_amdgcn_cvt_f32_fp8((int)codes[r * 128 + c], 0) * rs[r];
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(d[i]));
+  const float amax = pair_max(a);
+  const TileScale ts = tile_scale<POW2>(amax);
+  const bool scaled = __builtin_amdgcn_ballot_w64(ts.sx != 1.0f) != 0;
+  uint32_t packed[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float xv = d[4 * i + j];
+      if (scaled) xv *= ts.sx;
+      y[j] = div_rn(xv, ts.ss, ts.r);
+    }
+    packed[i] = pack4_e4m3(y[0], y[1], y[2], y[3]);
+  }
+  uint4* out = reinterpret_cast<uint4*>(qt + (kb * 128 + c) * M + mb * 128 + h * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    out[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+  if (h == 0) st[mb * K + kb * 128 + c] = ts.s;
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight blocks.  One workgroup per block (z = matrix, x = row block,
+// y = column block); each lane owns half a row (64 BF16 = 8 loads).  Block
+// amax: DPP row max, then across the 4 DPP rows of a wave and the 4 waves
+// through LDS.  Rows past N contribute nothing and are not written.
+// ---------------------------------------------------------------------------
+template <bool POW2>
+__global__ __launch_bounds__(256) void k_quantize_128x128(const uint16_t* __restrict__ w, int64_t N, int64_t K,
+                                                           uint8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ float part[16];
+  const int64_t nb = blockIdx.x, kb = blockIdx.y, g = blockIdx.z;
+  const int64_t NB = (N + 127) / 128, KT = K / 128;
+  const int t = threadIdx.x;
+  const int r = t >> 1, h = t & 1;
+  const int64_t row = nb * 128 + r;
+  const bool ok = row < N;
+  const uint16_t* src = w + (g * N + row) * K + kb * 128 + h * 64;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = ok ? reinterpret_cast<const uint4*>(src)[i] : make_uint4(0, 0, 0, 0);
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[i].x)), __builtin_fabsf(bf16_hi(v[i].x))));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[i].y)), __builtin_fabsf(bf16_hi(v[i].y))));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[i].z)), __builtin_fabsf(bf16_hi(v[i].z))));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[i].w)), __builtin_fabsf(bf16_hi(v[i].w))));
+  }
+  a = row16_max(a);
+  if ((t & 15) == 0) part[t >> 4] = a;
+  __syncthreads();
+  float amax = part[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) amax = __builtin_fmaxf(amax, part[i]);
+  const TileScale ts = tile_scale<POW2>(amax);
+  uint32_t packed[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint2 o = (ts.sx != 1.0f) ? quantize8<POW2, true>(v[i], ts) : quantize8<POW2, false>(v[i], ts);
+    packed[2 * i] = o.x;
+    packed[2 * i + 1] = o.y;
+  }
+  if (ok) {
+    uint4* out = reinterpret_cast<uint4*>(q + (g * N + row) * K + kb * 128 + h * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+  }
+  if (t == 0) s[(g * NB + nb) * KT + kb] = ts.s;
+}
+
+// ---------------------------------------------------------------------------
+// Elementwise FP32 -> E4M3 with the quantizers' encoding; NaN keeps its sign.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t cast4(float4 v) {
+  uint32_t w = pack4_e4m3(v.x, v.y, v.z, v.w);
+  const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (e[i] != e[i]) {
+      const uint32_t nan = 0x7Fu | ((__builtin_bit_cast(uint32_t, e[i]) >> 24) & 0x80u);
+      w = (w & ~(0xFFu << (8 * i))) | (nan << (8 * i));
+    }
+  }
+  return w;
+}
+
+__global__ __launch_bounds__(256) void k_cast_e4m3(const float* __restrict__ x, int64_t n, uint8_t* __restrict__ q) {
+  const int64_t n4 = n / 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    reinterpret_cast<uint32_t*>(q)[i] = cast4(reinterpret_cast<const float4*>(x)[i]);
+  // tail (n % 4 elements), one lane
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    for (int64_t i = n4 * 4; i < n; ++i) {
+      float4 v = make_float4(x[i], 0.f, 0.f, 0.f);
+      q[i] = (uint8_t)(cast4(v) & 0xFFu);
+    }
+  }
+}
+
+}  // namespace
+
+// ----------------------------- launchers ----------------------------------
+hipError_t launch_quantize_1x128(const void* x, int64_t M, int64_t K, uint8_t* q, float* s, bool pow2,
+                                 hipStream_t stream) {
+  const int64_t KT = K / 128;
+  dim3 grid((unsigned)((M + 15) / 16), (unsigned)((KT + kQ1Tiles - 1) / kQ1Tiles));
+  if (pow2)
+    hipLaunchKernelGGL(k_quantize_1x128<true>, grid, dim3(256), 0, stream, (const uint16_t*)x, M, K, q, s);
+  else
+    hipLaunchKernelGGL(k_quantize_1x128<false>, grid, dim3(256), 0, stream, (const uint16_t*)x, M, K, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_t128x1(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt, float* st,
+                                  bool pow2, hipStream_t stream) {
+  dim3 grid((unsigned)(M / 128), (unsigned)(K / 128));
+  if (pow2)
+    hipLaunchKernelGGL(k_quantize_t128x1<true>, grid, dim3(256), 0, stream, q, s, M, K, qt, st);
+  else
+    hipLaunchKernelGGL(k_quantize_t128x1<false>, grid, dim3(256), 0, stream, q, s, M, K, qt, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t K, uint8_t* q, float* s, bool pow2,
+                                   hipStream_t stream) {
+  dim3 grid((unsigned)((N + 127) / 128), (unsigned)(K / 128), (unsigned)G);
+  if (pow2)
+    hipLaunchKernelGGL(k_quantize_128x128<true>, grid, dim3(256), 0, stream, (const uint16_t*)w, N, K, q, s);
+  else
+    hipLaunchKernelGGL(k_quantize_128x128<false>, grid, dim3(256), 0, stream, (const uint16_t*)w, N, K, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream) {
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_cast_e4m3, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, q);
+  return hipGetLastError();
+}
+
+}  // namespace fp8bs

@@ -1,0 +1,205 @@
+/*
+ * fp8bs.h -- C ABI of libfp8bs: block-scaled FP8 GEMMs and the quantizers that
+ * feed them, hand-written for AMD Instinct MI355X (gfx950).
+ *
+ * Method (surveyed pages):
+ *   - page 1, the uniondaocoop.com board post that restates DeepSeek's FP8
+ *     mixed-precision training framework: fine-grained quantization with one
+ *     scale per 1x128 activation tile; FP8 GEMMs take FP8 inputs and write BF16
+ *     or FP32; partial sums are copied into FP32 registers at a fixed interval
+ *     along K; cached FP8 activations are converted from 1x128 to 128x1 tiles
+ *     for the backward pass.
+ *   - page 2, "A Deadly Mistake Uncovered on Deepseek China Ai ...": scaling
+ *     factors restricted to integral powers of two for some activations; the
+ *     request for MMA with per-group scaling.
+ *   - page 4, "Deepseek veroeffentlicht Deepgemm ...", section
+ *     "Schluesselmerkmale von DeepGemm": a dense layout and two MoE layouts.
+ *
+ * Formats.
+ *   E4M3  : OCP 8-bit float, 1 sign / 4 exponent (bias 7) / 3 mantissa bits, no
+ *           infinities, 0x7F/0xFF = NaN, largest finite 448.  Stored as bytes.
+ *   BF16  : 16-bit brain float (upper half of a binary32), stored as uint16.
+ *   Scales: binary32.
+ *
+ * Quantization rule (every quantizer; readings of points the pages leave
+ * open): per tile, amax = max |x|; s = 1 if amax == 0, else
+ * max(fl32(amax / 448), 2^-149) with a correctly rounded FP32 divide; with
+ * FP8BS_SCALE_POW2, s is rounded up to the next power of two; every element is
+ * encoded as E4M3(fl32(x / s)), round-to-nearest-even, saturating to +-448.
+ * Results are bit-exact functions of the inputs.  Inputs must be finite.
+ *
+ * GEMM rule: D = A * B^T ("NT": both operands K-contiguous) with
+ *   D[m][n] = sum over 128-wide K chunks kb of
+ *             sA[kb][m] * sB[n/128][kb] * (sum_{k in kb} A[m][k] * B[n][k])
+ * Each chunk's inner sum is formed in FP32 by the matrix cores and promoted
+ * into a separate FP32 accumulator with its scale product (the pages'
+ * promotion interval, here 128).  Output: BF16 (round-to-nearest-even) or
+ * FP32.  Summation order differs from a plain dot product, so results agree
+ * with an exact reference to within |d - ref| <= 8e-3 |ref| + 1e-3 rms(ref).
+ *
+ * Conventions shared by every entry point.
+ *   - Pointers are device pointers (memory the current HIP device can read or
+ *     write) unless stated otherwise; data pointers must be 16-byte aligned.
+ *   - All tensors are dense row-major with no padding between rows.
+ *   - The caller allocates, owns and frees every buffer; the library keeps no
+ *     pointer after returning, allocates nothing, and has no workspace.
+ *   - Every call enqueues its kernels on `stream` (NULL = the null stream) and
+ *     returns without waiting; buffers must stay alive until the stream work
+ *     completes.  Calls are re-entrant and thread-safe.
+ *   - Arguments are checked before anything is launched; on any error nothing
+ *     is launched and no memory is written.  Check order: sizes
+ *     (FP8BS_ERR_SHAPE), flags / output dtype (FP8BS_ERR_FLAGS); then an empty
+ *     problem (zero rows, columns or groups) returns FP8BS_OK without
+ *     launching and may pass NULL pointers; otherwise null pointers
+ *     (FP8BS_ERR_NULL), 16-byte alignment (FP8BS_ERR_ALIGN; the int32 group
+ *     arrays need only 4), the current device (FP8BS_ERR_DEVICE).  The HIP
+ *     runtime's last-error state is cleared before launching; a launch it
+ *     rejects returns FP8BS_ERR_LAUNCH.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BS_ABI_VERSION 1
+
+/* Same type as hipStream_t; declared here so the header needs no HIP headers. */
+struct ihipStream_t;
+typedef struct ihipStream_t* fp8bs_stream_t;
+
+typedef enum {
+  FP8BS_OK = 0,
+  FP8BS_ERR_NULL = 1,   /* a required pointer is NULL                        */
+  FP8BS_ERR_SHAPE = 2,  /* a size is negative or breaks a divisibility rule  */
+  FP8BS_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned                  */
+  FP8BS_ERR_FLAGS = 4,  /* unknown flag bits or output dtype                 */
+  FP8BS_ERR_DEVICE = 5, /* no current HIP device, or it is not gfx950        */
+  FP8BS_ERR_LAUNCH = 6  /* the HIP runtime rejected a kernel launch          */
+} fp8bs_status;
+
+/* Output dtypes of the GEMMs. */
+enum { FP8BS_OUT_BF16 = 0, FP8BS_OUT_FP32 = 1 };
+
+/* Quantizer flags. */
+enum { FP8BS_SCALE_POW2 = 1u };
+
+/*
+ * 1x128 activation quantization (page 1, paragraph on fine-grained tiles).
+ *   x  : BF16 [M][K]            (input)
+ *   q  : E4M3 [M][K]            (output)
+ *   s  : FP32 [K/128][M]        (output; tile (m, kb) -> s[kb][m])
+ * Requires M >= 0, K > 0, K % 128 == 0.  flags: 0 or FP8BS_SCALE_POW2.
+ */
+fp8bs_status fp8bs_quantize_1x128(const void* x, int64_t M, int64_t K,
+                                  uint8_t* q, float* s, uint32_t flags,
+                                  fp8bs_stream_t stream);
+
+/*
+ * 1x128 -> 128x1 transpose-requantize of a cached FP8 activation (page 1,
+ * paragraph on FP8 activation caching and the backward-pass tile conversion).
+ * Each value is dequantized as d = fl32(E4M3(q) * s[kb][m]); every column k
+ * of each 128-row block mb is then requantized with the quantization rule and
+ * written transposed, so the new tiles are contiguous rows of qt.
+ *   q  : E4M3 [M][K],  s  : FP32 [K/128][M]        (input, 1x128 tiles)
+ *   qt : E4M3 [K][M],  st : FP32 [M/128][K]        (output; tile (k, mb) ->
+ *                                                    st[mb][k])
+ * Requires M >= 0, K >= 0, M % 128 == 0, K % 128 == 0.
+ */
+fp8bs_status fp8bs_quantize_transpose_128x1(const uint8_t* q, const float* s,
+                                            int64_t M, int64_t K,
+                                            uint8_t* qt, float* st,
+                                            uint32_t flags,
+                                            fp8bs_stream_t stream);
+
+/*
+ * 128x128 block quantization of (optionally batched) weights: one scale per
+ * block of up to 128 rows x 128 columns; a partial last row block uses its
+ * valid rows only.  Weights for the GEMMs below are laid out this way.
+ *   w  : BF16 [G][N][K]                     (input; G = 1 for one matrix)
+ *   q  : E4M3 [G][N][K]                     (output)
+ *   s  : FP32 [G][ceil(N/128)][K/128]       (output)
+ * Requires G >= 0, N >= 0, K > 0, K % 128 == 0.
+ */
+fp8bs_status fp8bs_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t K,
+                                    uint8_t* q, float* s, uint32_t flags,
+                                    fp8bs_stream_t stream);
+
+/*
+ * Dense block-scaled FP8 GEMM (page 1, paragraphs on FP8 GEMM inputs/outputs
+ * and FP32 promotion; page 4, section "Schluesselmerkmale von DeepGemm",
+ * dense layout).  D = A * B^T.
+ *   a  : E4M3 [M][K],   sa : FP32 [K/128][M]              (1x128 tiles)
+ *   b  : E4M3 [N][K],   sb : FP32 [ceil(N/128)][K/128]    (128x128 blocks)
+ *   d  : [M][N], BF16 (out_dtype = FP8BS_OUT_BF16) or FP32 (FP8BS_OUT_FP32)
+ * Requires M >= 0, N >= 0, N % 16 == 0, K > 0, K % 128 == 0.
+ */
+fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa,
+                                        const uint8_t* b, const float* sb,
+                                        void* d, int64_t M, int64_t N, int64_t K,
+                                        int32_t out_dtype, fp8bs_stream_t stream);
+
+/*
+ * Grouped GEMM, contiguous MoE layout (page 4, section "Schluesselmerkmale
+ * von DeepGemm", the first of the two MoE layouts): the rows of every group
+ * are concatenated; group g owns rows [m_offsets[g], m_offsets[g+1]) of A and
+ * D and uses weight matrix b[g] with scales sb[g].
+ *   a  : E4M3 [Mt][K],   sa : FP32 [K/128][Mt]
+ *   b  : E4M3 [G][N][K], sb : FP32 [G][ceil(N/128)][K/128]
+ *   d  : [Mt][N] BF16 or FP32
+ *   m_offsets : int32 [G+1], DEVICE memory, read on the device only (the call
+ *               never synchronizes).  Must be non-decreasing with m_offsets[0]
+ *               == 0, every difference a multiple of 128, m_offsets[G] <= Mt;
+ *               violations are not detected and give undefined results.  Rows
+ *               at or past m_offsets[G] are not written.  Empty groups are
+ *               allowed.
+ * Requires G >= 0, Mt >= 0, Mt % 128 == 0, N % 16 == 0, K > 0, K % 128 == 0.
+ */
+fp8bs_status fp8bs_grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa,
+                                               const uint8_t* b, const float* sb,
+                                               void* d, const int32_t* m_offsets,
+                                               int32_t G, int64_t Mt, int64_t N, int64_t K,
+                                               int32_t out_dtype, fp8bs_stream_t stream);
+
+/*
+ * Grouped GEMM, masked MoE layout for decoding (page 4, the second MoE layout;
+ * page 2, paragraph on decoding: a few hundred tokens per expert at most, so
+ * the step is bound by memory, not compute): every group has a fixed
+ * capacity of rows and a valid count that lives on the device.
+ *   a  : E4M3 [G][cap][K],  sa : FP32 [G][K/128][cap]
+ *   b  : E4M3 [G][N][K],    sb : FP32 [G][ceil(N/128)][K/128]
+ *   d  : [G][cap][N] BF16 or FP32
+ *   masked_m : int32 [G], DEVICE memory, read on the device only; values are
+ *              clamped to [0, cap].  Rows at or past masked_m[g] of group g
+ *              are neither used nor written (d keeps its previous contents).
+ * Requires G >= 0, cap >= 0, N % 16 == 0, K > 0, K % 128 == 0.
+ */
+fp8bs_status fp8bs_grouped_gemm_fp8_masked(const uint8_t* a, const float* sa,
+                                           const uint8_t* b, const float* sb,
+                                           void* d, const int32_t* masked_m,
+                                           int32_t G, int64_t cap, int64_t N, int64_t K,
+                                           int32_t out_dtype, fp8bs_stream_t stream);
+
+/*
+ * Elementwise FP32 -> E4M3 cast with the encoding used by every quantizer
+ * (round-to-nearest-even, +-inf and finite overflow saturate to +-448, the
+ * sign of zero is kept, NaN maps to the NaN code of the same sign).
+ *   x : FP32 [n] (input),  q : E4M3 [n] (output).  Requires n >= 0.
+ */
+fp8bs_status fp8bs_cast_f32_to_e4m3(const float* x, int64_t n, uint8_t* q,
+                                    fp8bs_stream_t stream);
+
+/* Static, NUL-terminated description of a status code (host memory). */
+const char* fp8bs_status_str(fp8bs_status status);
+
+/* FP8BS_ABI_VERSION of the built library. */
+int32_t fp8bs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

@@ -98,6 +98,18 @@ def gemm_sample_f64(a, sa, b, sb, rows, cols) -> np.ndarray:
     return np.sum(A * B, axis=1)
 
 
+def gemm_block_f64(a, sa, b, sb, rows, cols) -> np.ndarray:
+    """float64 D[rows][:, cols]: the outputs at every (row, col) pair of the
+    sampled rows and columns (dequantize only those rows of A and of B)."""
+    rows = np.asarray(rows, np.int64)
+    cols = np.asarray(cols, np.int64)
+    A = dequant_a(np.asarray(a)[rows], np.asarray(sa)[:, rows])
+    Bq = np.asarray(b)[cols]
+    Bs = np.asarray(sb)[cols // TILE]
+    B = e4m3.decode(Bq) * np.repeat(Bs.astype(np.float64), TILE, axis=1)
+    return A @ B.T
+
+
 def grouped_contiguous_f64(a, sa, b, sb, m_offsets) -> np.ndarray:
     """Contiguous layout: D[Mt][N] float64, NaN on rows outside every group."""
     a = np.asarray(a, np.uint8)

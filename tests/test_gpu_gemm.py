@@ -1,0 +1,118 @@
+"""GPU parity of the dense block-scaled GEMM against the CPU oracle.
+
+Inputs: the seeded workload recipe quantized by the oracle (the same bytes go
+to both sides).  Bar: |gpu - ref| <= 8e-3 |ref| + 1e-3 rms(ref) elementwise,
+ref = float64 definition rounded once to the output dtype; bit-exact when the
+exact result is representable in FP32 at every step (exact-integer inputs).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_block_scaled_04_amd import fp8bs, synth
+from oracle import bf16, e4m3, gemm, quantize
+from tests.gpu_util import (assert_codes_equal, assert_gemm_close, codes_dev, f32_dev, out_host_f64,
+                            require_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    require_gpu()
+
+
+def operands(M, N, K, seed, pow2=False):
+    w = synth.dense(M, N, K, seed=seed)
+    a, sa = quantize.quantize_1x128(w["a"], pow2)
+    b, sb = quantize.quantize_128x128(w["b"], pow2)
+    return a, sa, b, sb
+
+
+def run(a, sa, b, sb, out_dtype=torch.bfloat16):
+    d = fp8bs.gemm(codes_dev(a), f32_dev(sa), codes_dev(b), f32_dev(sb), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return d
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (1, 16, 128), (37, 48, 384), (130, 2112, 256),
+                                   (256, 272, 1024), (64, 4096, 128), (300, 400, 640), (513, 144, 1152)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_gemm_workload_recipe(M, N, K, out_dtype):
+    print(f"gemm M={M} N={N} K={K} out={out_dtype}", flush=True)
+    a, sa, b, sb = operands(M, N, K, seed=M + 7 * N + K)
+    d = run(a, sa, b, sb, out_dtype)
+    ref = gemm.gemm_f64(a, sa, b, sb)
+    ref = (bf16.to_f32(gemm.round_out(ref, "bf16")) if out_dtype == torch.bfloat16
+           else gemm.round_out(ref, "f32")).astype(np.float64)
+    assert_gemm_close(out_host_f64(d), ref, f"gemm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_gemm_exact_integer_inputs_bit_exact(out_dtype):
+    # codes with integer values in [-16, 16] and power-of-two scales: every
+    # partial sum is exact in FP32, so the output is the one rounding of the
+    # exact result.
+    rng = np.random.default_rng(0)
+    vals = e4m3.decode(np.arange(256, dtype=np.uint8))
+    ints = np.array([c for c in range(256) if np.isfinite(vals[c]) and vals[c] == np.round(vals[c])
+                     and abs(vals[c]) <= 16 and c != 0x80], np.uint8)
+    M, N, K = 256, 272, 1024
+    a = rng.choice(ints, (M, K)).astype(np.uint8)
+    b = rng.choice(ints, (N, K)).astype(np.uint8)
+    sa = (2.0 ** rng.integers(-2, 2, (K // 128, M))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-2, 2, (3, K // 128))).astype(np.float32)
+    d = run(a, sa, b, sb, out_dtype)
+    ref = gemm.gemm_ref(a, sa, b, sb, "bf16" if out_dtype == torch.bfloat16 else "f32")
+    got = d.view(torch.int16).cpu().numpy().view(np.uint16) if out_dtype == torch.bfloat16 \
+        else d.cpu().numpy().view(np.uint32)
+    assert_codes_equal(got, ref.view(got.dtype), "exact-integer gemm")
+
+
+def test_gemm_identity_weights():
+    x = synth.activation(256, 384, seed=4)["a"]
+    a, sa = quantize.quantize_1x128(x)
+    b = np.zeros((384, 384), np.uint8)
+    b[np.arange(384), np.arange(384)] = 0x38
+    sb = np.ones((3, 3), np.float32)
+    d = run(a, sa, b, sb, torch.float32)
+    # one nonzero product per output: D = fl32(dec(a) * sa); the kernel's
+    # accumulator starts at +0, so a -0 product comes out as +0
+    want = gemm.dequant_a(a, sa).astype(np.float32) + np.float32(0.0)
+    assert_codes_equal(d.cpu().numpy().view(np.uint32), want.view(np.uint32), "identity weights")
+
+
+def test_gemm_writes_only_its_output():
+    M, N, K = 130, 48, 256
+    a, sa, b, sb = operands(M, N, K, seed=9)
+    buf = torch.full((M * N + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = buf[2048:2048 + M * N].view(M, N)
+    fp8bs.gemm(codes_dev(a), f32_dev(sa), codes_dev(b), f32_dev(sb), out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:2048]).all() and torch.isnan(buf[2048 + M * N:]).all()
+    ref = bf16.to_f32(gemm.gemm_ref(a, sa, b, sb)).astype(np.float64)
+    assert_gemm_close(out_host_f64(out), ref, "in-place out")
+
+
+def test_gemm_training_projection_full_size_sampled():
+    # 4096 x 2112 x 7168: the last 128-wide column tile holds only 64 valid
+    # columns (ragged weight block).  Sampled rows x columns, incl. the tails.
+    M, N, K = 4096, 2112, 7168
+    print("gemm full size 4096x2112x7168", flush=True)
+    a, sa, b, sb = operands(M, N, K, seed=0)
+    d = run(a, sa, b, sb)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(M - 16, M), rng.integers(0, M, 96)]))
+    cols = np.unique(np.concatenate([np.arange(0, 16), np.arange(N - 80, N), rng.integers(0, N, 160)]))
+    ref = bf16.to_f32(bf16.from_f64_rne(gemm.gemm_block_f64(a, sa, b, sb, rows, cols))).astype(np.float64)
+    got = out_host_f64(d)[np.ix_(rows, cols)]
+    assert_gemm_close(got, ref, "gemm 4096x2112x7168")
+
+
+def test_gemm_decode_shape_pow2_full():
+    M, N, K = 128, 24576, 1536
+    print("gemm decode 128x24576x1536 pow2", flush=True)
+    a, sa, b, sb = operands(M, N, K, seed=0, pow2=True)
+    d = run(a, sa, b, sb)
+    ref = bf16.to_f32(gemm.gemm_ref(a, sa, b, sb)).astype(np.float64)
+    assert_gemm_close(out_host_f64(d), ref, "gemm 128x24576x1536")

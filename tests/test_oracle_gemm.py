@@ -108,6 +108,8 @@ def test_two_exact_paths_agree_on_workload_recipe():
     rows = np.array([0, 5, 63, 17])
     cols = np.array([199, 0, 128, 127])
     assert np.allclose(gemm.gemm_sample_f64(a, sa, b, sb, rows, cols), d1[rows, cols], rtol=1e-14, atol=0)
+    blk = gemm.gemm_block_f64(a, sa, b, sb, rows, cols)
+    assert np.allclose(blk, d1[np.ix_(rows, cols)], rtol=1e-14, atol=0)
 
 
 def test_grouped_contiguous_is_dense_per_group():
