@@ -91,11 +91,13 @@ __device__ __forceinline__ TileScale tile_scale(float amax) {
   return t;
 }
 
+// s > 0, so the quotient has the sign of x.  The correction step alone would
+// turn x = -0 into +0 (fma(+0, r, -0) = +0), hence the copysign.
 __device__ __forceinline__ float div_rn(float x, float s, float r) {
 #pragma clang fp contract(off)
   float q = x * r;
   float e = __builtin_fmaf(-q, s, x);
-  return __builtin_fmaf(e, r, q);
+  return __builtin_copysignf(__builtin_fmaf(e, r, q), x);
 }
 
 // ---------------------------------------------------------------------------

@@ -14,19 +14,28 @@
 //   * One chunk of 128 K is exactly one v_mfma_f32_16x16x128_f8f6f4 per 16x16
 //     output block, issued with a zero accumulator, so the MFMA result is the
 //     chunk partial P in FP32.  The VALU then folds it into a second FP32
-//     accumulator set with one FMA per element: acc += P * (sA * sB).  MFMA and
-//     VALU are separate pipes, so the promotion overlaps the next MFMAs.
+//     accumulator set with one FMA per element: acc += P * (sA * sB).  The
+//     MFMA of block b is issued before the FMAs of block b-1, so the VALU
+//     works while the matrix core runs.
 //   * The MFMA is issued with the weights as its first operand and the
 //     activations as its second, i.e. it produces D^T blocks.  A lane then
 //     holds four consecutive n of one m: the four values share one sA (per
 //     lane) and one sB (per wave), so the scale is a single multiply per
 //     16x16 block and the BF16 store is one 8-byte write.
-//   * Workgroup: 256 lanes = 4 waves in a 2x2 grid; tile BM x BN, wave tile
-//     BM/2 x BN/2.  A and B chunks (BM x 128 and BN x 128 bytes) and the BM
-//     activation scales are streamed straight from HBM into LDS with 16-byte
-//     global_load_lds (no VGPR staging), double buffered.  Rows are 128 bytes;
-//     each 16-byte segment is XOR-swizzled by row so that the 16 lanes of an
-//     MFMA fragment read hit distinct LDS banks.
+//   * Operand traffic sets the tile: L2 feeds a CU about 37 bytes per clock
+//     (measured), a 16x16x128 MFMA takes 32 clocks per SIMD, so a tile must
+//     load at most ~300 bytes per MFMA to keep the matrix cores busy.  A
+//     256x256 tile loads 256 bytes per MFMA (8 waves, two per SIMD, wave tile
+//     64x128); 128x128 (4 waves, 64x64 each) loads 512 and serves the shapes
+//     that have too few 256x256 tiles to fill 256 CUs.
+//   * A and B chunks (BM x 128 and BN x 128 bytes) and the chunk's scales are
+//     streamed straight from memory into LDS with buffer_load ... lds (no
+//     VGPR staging; the K offset is a scalar), two stages, in whole 128-byte
+//     rows with a swizzle that lets MFMA fragments read LDS at close to its
+//     full rate.  The DMA of the next
+//     chunk starts right after each step's barrier.  The small tile also
+//     double-buffers its MFMA fragments in registers; the large one holds
+//     half of its weight fragments at a time.
 //   * Workgroup ids are renumbered so that tiles sharing operand panels run
 //     on the same XCD (own L2), then walked in groups of GROUP_M tile rows.
 #include "device_common.h"
@@ -37,27 +46,101 @@ namespace {
 
 constexpr int kKC = 128;  // K chunk = promotion interval = MFMA K
 
-template <int BM, int BN>
-struct TileCfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;
+template <int BM_, int BN_, int WGM_, int WGN_, bool DB_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr bool DB = DB_;                   // fragments double buffered in registers
+  static constexpr int NW = WGM * WGN;              // waves per workgroup
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int FM = WM / 16, FN = WN / 16;  // 16x16 fragments per wave
   static constexpr int A_BYTES = BM * kKC;
   static constexpr int B_BYTES = BN * kKC;
-  static constexpr int SA_BYTES = BM * 4;
-  static constexpr int SB_BYTES = 256;     // weight scales of the chunk (first BN/128 used)
-  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-  static constexpr int A_LOADS = BM / 32;  // 8 rows per wave instruction, 4 waves
-  static constexpr int B_LOADS = BN / 32;
-  static constexpr int SA_WAVES = BM / 64; // 64 scales per dword-DMA instruction
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must be a multiple of 64");
-  static_assert(SA_WAVES < 4, "one wave must be free to fetch the weight scales");
-  static_assert(WN <= 128, "a wave's columns must share one 128-row weight block");
+  // One scale DMA per wave and chunk (64 floats): slots 0..BM/64-1 hold the
+  // activation scales of the tile's rows, slot BM/64 the weight scales of
+  // weight block rows n0/128 + i; any further slots hold copies of it.
+  static constexpr int SA_WAVES = BM / 64;
+  static constexpr int SC_BYTES = NW * 256;
+  static constexpr int SA_OFF = A_BYTES + B_BYTES;
+  static constexpr int SB_OFF = A_BYTES + B_BYTES + SA_WAVES * 256;
+  static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int A_LOADS = BM / (8 * NW);     // 8 rows of 128 bytes per wave instruction
+  static constexpr int B_LOADS = BN / (8 * NW);
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "rows must split evenly over the waves");
+  static_assert(SA_WAVES < NW, "one wave must be left for the weight scales");
+  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-row weight block");
+  static_assert(LDS_BYTES <= 160 * 1024, "two stages must fit in LDS");
 };
 
-// 16-byte segment swizzle of an LDS row: rows r and r+1 live in different
-// halves of a 256-byte bank line, and (r >> 1) & 7 spreads 16 consecutive rows
-// over 8 segments of each half.
+using SmallTile = Cfg<128, 128, 2, 2, true>;
+using LargeTile = Cfg<256, 256, 4, 2, false>;
+
+// LDS layout of an operand chunk: rows of 128 bytes (one K chunk), row-major,
+// with the 16-byte segments of row r XOR-swizzled: logical segment s is
+// stored at segment s ^ swz(r), swz(r) = (r >> 1) & 7.  An MFMA fragment of
+// 16 rows has lane l = fr + 16*fg hold row fr's logical segments fg and
+// fg + 4 (the order of K inside a fragment is free as long as both operands
+// use the same one).  Measured on gfx950 with 8 waves per CU, this pairing
+// reads at 227 of 256 B/clk per CU; the pairing (2fg, 2fg+1) stays below 145
+// with any of the swizzles tried, and unswizzled rows reach 81.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// Buffer resource word 3 for raw (untyped) dword access on gfx9-class parts.
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// A raw buffer resource (stride 0) over [base, base + bytes), built from
+// readfirstlane'd fields so it lives in SGPRs.
+__device__ __forceinline__ v4i make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const int64_t nb = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes;
+  v4i r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane((int)nb);
+  r.w = kRsrcWord3;
+  return r;
+}
+
+// Memory -> LDS DMA of 16 (4) bytes per lane: lane l's data lands at LDS byte
+// address lds + 16*l (4*l); the source is rsrc.base + voff + soff, and the
+// hardware range check on voff against the descriptor's size turns
+// out-of-range lanes into zeros without a memory access.
+//
+// Issued from inline asm on purpose: the compiler, seeing an LDS DMA, would
+// make every later LDS read wait for all outstanding DMA (it cannot tell the
+// two LDS stages apart), which would serialise the pipeline.  Hidden in asm,
+// the DMA is ordered by the "memory" clobber and waited for explicitly with
+// s_waitcnt at the top of each step.  The asm sets M0 (the LDS destination);
+// nothing else in these kernels uses M0.  There are no output registers.
+// The scalar operands go through readfirstlane (free for values already in
+// SGPRs) so the "s" constraints always get SGPRs.
+__device__ __forceinline__ v4i uniform(v4i r) {
+  return v4i{__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+             __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w)};
+}
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform(rsrc)),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
+}
+__device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform(rsrc)),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0): vector memory loads complete in issue order,
+// so all but the N most recent have landed.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p);
+}
 
 struct GemmArgs {
   const uint8_t* a;
@@ -68,23 +151,34 @@ struct GemmArgs {
   const int32_t* groups;
   int64_t M, N, K;
   int32_t G;
-  int32_t tiles_m, tiles_n;
+  int32_t tiles_m, tiles_n;   // tile grid (contiguous: Mt/BM + G virtual m-tiles)
   int32_t group_m;
 };
 
-template <int BM, int BN, int MODE, bool OUT_F32>
-__global__ __launch_bounds__(256) void k_gemm(const GemmArgs p) {
-  using C = TileCfg<BM, BN>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];
+template <int FM, int FN>
+struct Frags {
+  v8i a[FM];
+  v8i b[FN];
+  float sa[FM];
+  float sb;
+};
+
+template <class C, int MODE, bool OUT_F32>
+__global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
+  // The body uses AMDGPU buffer descriptors, which exist in the device pass
+  // only; the host pass needs just the kernel's signature for its launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = C::BM, BN = C::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int64_t K = p.K, N = p.N;
   const int KT = (int)(K / kKC);
   const int64_t NB = (N + 127) / 128;
 
-  // ---- tile -> (group, tm, tn) -------------------------------------------
+  // ---- tile -> (group, rows, columns) ------------------------------------
   const int total = (int)gridDim.x;
   const int pid = xcd_remap((int)blockIdx.x, total);
   int g = 0, tm, tn;
@@ -103,23 +197,37 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs p) {
     tm = first_m + r % gsz;
     tn = r / gsz;
   }
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t n0 = (int64_t)tn * BN;
+  int64_t m0 = (int64_t)tm * BM;
 
   const uint8_t* a_base = p.a;
   const float* sa_base = p.sa;
   const uint8_t* b_base = p.b;
   const float* sb_base = p.sb;
-  int64_t m_alloc = p.M;     // rows that exist in memory (loads are clamped to them)
-  int64_t m_valid = p.M;     // rows that are computed and stored
-  int64_t sa_stride = p.M;   // distance between consecutive K chunks in sA
-  int64_t d_row0 = 0;        // first output row of this group's block of D
+  int64_t m_alloc = p.M;           // rows that exist in memory (loads are clamped to them)
+  int64_t m_valid = p.M;           // rows that are computed and stored
+  const int64_t sa_stride = p.M;   // distance between consecutive K chunks in sA
+  int64_t d_row0 = 0;              // first output row of this group's block of D
   if (MODE == kContiguous) {
+    // Tiles are laid out per group (group boundaries are only multiples of
+    // 128): virtual m-tile tm is tile t of group g, where tm = (tile counts
+    // of the groups before g) + t.
     const int32_t* offs = p.groups;
-    if (m0 >= offs[p.G]) return;
-    int gg = 0;
-    while (gg + 1 < p.G && offs[gg + 1] <= m0) ++gg;
-    g = gg;
-    m_valid = offs[g + 1];
+    int first = 0;
+    bool found = false;
+    for (int gg = 0; gg < p.G; ++gg) {
+      const int64_t lo = offs[gg], hi = offs[gg + 1];
+      const int cnt = (int)((hi - lo + BM - 1) / BM);
+      if (tm < first + cnt) {
+        g = gg;
+        m0 = lo + (int64_t)(tm - first) * BM;
+        m_valid = hi;
+        found = true;
+        break;
+      }
+      first += cnt;
+    }
+    if (!found) return;
     b_base += (int64_t)g * N * K;
     sb_base += (int64_t)g * NB * KT;
   } else if (MODE == kMasked) {
@@ -133,61 +241,98 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs p) {
     sb_base += (int64_t)g * NB * KT;
     d_row0 = (int64_t)g * p.M;
   }
-  const uint8_t* a_tile = a_base + m0 * K;
-  const uint8_t* b_tile = b_base + n0 * K;
 
-  // ---- per-lane DMA sources (byte offsets from the tile base) ------------
-  uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
-#pragma unroll
-  for (int i = 0; i < C::A_LOADS; ++i) {
-    const int row = (i * 4 + wave) * 8 + (lane >> 3);
-    const int seg = (lane & 7) ^ swz(row);
-    int64_t gr = m0 + row;
-    if (gr > m_alloc - 1) gr = m_alloc - 1;
-    a_off[i] = (uint32_t)((gr - m0) * K + seg * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < C::B_LOADS; ++i) {
-    const int row = (i * 4 + wave) * 8 + (lane >> 3);
-    const int seg = (lane & 7) ^ swz(row);
-    int64_t gr = n0 + row;
-    if (gr > N - 1) gr = N - 1;
-    b_off[i] = (uint32_t)((gr - n0) * K + seg * 16);
-  }
-  int64_t sa_row = m0 + wave * 64 + lane;
+  // ---- buffer resources (SGPRs) and per-lane DMA offsets ------------------
+  const int64_t a_rows = min<int64_t>(m_alloc - m0, BM);
+  const int64_t b_rows = min<int64_t>(N - n0, BN);
+  const v4i ra = make_rsrc(a_base + m0 * K, a_rows * K);
+  const v4i rb = make_rsrc(b_base + n0 * K, b_rows * K);
+  const v4i rsa = make_rsrc(sa_base, KT * sa_stride * 4);
+  const v4i rsb = make_rsrc(sb_base, NB * KT * 4);
+
+  // DMA instruction t = i*NW + wave moves rows 8t .. 8t+7 (whole 128-byte
+  // lines), lane l taking row 8t + l/8, physical segment l%8, i.e. logical
+  // segment (l%8) ^ swz(row).  With NW even, swz(row) = 4*(wave&1) + l/16
+  // for every instruction of the wave, so one base offset serves all of them
+  // for both operands.  The row stays in the vector offset, where the
+  // hardware range check sees it: rows past the end of A or B (a ragged last
+  // tile) are out of range and read as zeros.
+  static_assert(C::NW % 2 == 0, "the DMA mapping needs an even number of waves");
+  const uint32_t row_off = (uint32_t)(((wave * 8 + (lane >> 3)) * K) +
+                                      (((lane & 7) ^ (((wave & 1) << 2) + (lane >> 4))) * 16));
+  const uint32_t row_step = (uint32_t)(C::NW * 8 * K);
+  // Scale DMA of this wave (one dword per lane per chunk, no branches):
+  // waves below SA_WAVES fetch activation scales of rows m0 + 64*wave + lane,
+  // the others the weight scale of block row n0/128 + lane (both clamped).
+  const bool sa_wave = wave < C::SA_WAVES;
+  int64_t sa_row = m0 + (sa_wave ? wave : 0) * 64 + lane;
   if (sa_row > m_alloc - 1) sa_row = m_alloc - 1;
-  // weight scales: lane l of the last wave fetches the scale of weight block
-  // row n0/128 + l (clamped), so LDS holds this tile's sB values per chunk.
   int64_t sb_blk = n0 / 128 + lane;
   if (sb_blk > NB - 1) sb_blk = NB - 1;
-  const float* sb_lane = sb_base + sb_blk * KT;
+  const v4i rsc = sa_wave ? rsa : rsb;
+  const uint32_t sc_voff = sa_wave ? (uint32_t)(sa_row * 4) : (uint32_t)(sb_blk * KT * 4);
+  const uint32_t sc_step = __builtin_amdgcn_readfirstlane(sa_wave ? (uint32_t)(sa_stride * 4) : 4u);
 
+  // Chunks past the end (the pipeline issues ahead) use descriptors with
+  // zero records: every lane is out of range, so the hardware writes zeros
+  // to LDS and reads no memory.
+  const v4i r_none = make_rsrc(p.a, 0);
+  const uint32_t smem_lds = lds_addr(smem);
   auto issue = [&](int kb, int stage) {
-    uint8_t* st = smem + stage * C::STAGE;
-    const uint8_t* ak = a_tile + (int64_t)kb * kKC;
-    const uint8_t* bk = b_tile + (int64_t)kb * kKC;
+    const uint32_t st = smem_lds + stage * C::STAGE;
+    const bool live = kb < KT;
+    const uint32_t koff = live ? (uint32_t)kb * kKC : 0u;
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(live ? (uint32_t)kb * sc_step : 0u);
+    const v4i rak = live ? ra : r_none;
+    const v4i rbk = live ? rb : r_none;
+    const v4i rck = live ? rsc : r_none;
+    // Recomputed per chunk (one add per instruction) rather than kept live:
+    // the opaque copy stops the compiler from hoisting them into registers.
+    uint32_t ro = row_off;
+    asm volatile("" : "+v"(ro));
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(ak + a_off[i]),
-                                       (lds_void*)(st + (i * 4 + wave) * 8 * kKC), 16, 0, 0);
+      dma16(rak, st + (i * C::NW + wave) * 8 * kKC, ro + i * row_step, koff);
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(bk + b_off[i]),
-                                       (lds_void*)(st + C::A_BYTES + (i * 4 + wave) * 8 * kKC), 16, 0, 0);
-    if (wave < C::SA_WAVES)
-      __builtin_amdgcn_global_load_lds((const void*)(sa_base + (int64_t)kb * sa_stride + sa_row),
-                                       (lds_void*)(st + C::A_BYTES + C::B_BYTES + wave * 256), 4, 0, 0);
-    if (wave == 3)
-      __builtin_amdgcn_global_load_lds((const void*)(sb_lane + kb),
-                                       (lds_void*)(st + C::A_BYTES + C::B_BYTES + C::SA_BYTES), 4, 0, 0);
+      dma16(rbk, st + C::A_BYTES + (i * C::NW + wave) * 8 * kKC, ro + i * row_step, koff);
+    dma4(rck, st + C::SA_OFF + wave * 256, sc_voff, soff);
   };
-
+  constexpr int DMA_PER_CHUNK = C::A_LOADS + C::B_LOADS + 1;   // vmcnt of one issue()
   // ---- per-lane fragment read offsets -----------------------------------
   const int fr = lane & 15, fg = lane >> 4;
-  const uint32_t rd0 = fr * kKC + 16 * ((2 * fg) ^ swz(fr));
-  const uint32_t rd1 = fr * kKC + 16 * ((2 * fg + 1) ^ swz(fr));
+  const uint32_t rd0 = fr * kKC + 16 * (fg ^ swz(fr));
+  const uint32_t rd1 = fr * kKC + 16 * ((fg + 4) ^ swz(fr));
   const int a_row0 = wm * C::WM, b_row0 = wn * C::WN;
   const int sb_idx = (int)((n0 + b_row0) / 128 - n0 / 128);   // this wave's weight block in the tile
+
+  // With fragments double buffered a wave holds every weight fragment of the
+  // chunk; otherwise it holds half of them at a time (FNH).
+  constexpr int FNH = C::DB ? C::FN : C::FN / 2;
+  using F = Frags<C::FM, FNH>;
+  auto read_a = [&](int stage, F& f) {
+    const uint8_t* st = smem + stage * C::STAGE;
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) {
+      const uint8_t* base = st + (a_row0 + 16 * j) * kKC;
+      const uint4 lo = *reinterpret_cast<const uint4*>(base + rd0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(base + rd1);
+      f.a[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      f.sa[j] = reinterpret_cast<const float*>(st + C::SA_OFF)[a_row0 + 16 * j + fr];
+    }
+    f.sb = reinterpret_cast<const float*>(st + C::SB_OFF)[sb_idx];
+  };
+  // weight fragments i0 .. i0+FNH-1 of the wave
+  auto read_b = [&](int stage, F& f, int i0) {
+    const uint8_t* st = smem + stage * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < FNH; ++i) {
+      const uint8_t* base = st + C::A_BYTES + (b_row0 + 16 * (i0 + i)) * kKC;
+      const uint4 lo = *reinterpret_cast<const uint4*>(base + rd0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(base + rd1);
+      f.b[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+  };
 
   v4f acc[C::FN][C::FM];
 #pragma unroll
@@ -195,55 +340,108 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
-  for (int kb = 0; kb < KT; ++kb) {
-    const int stage = kb & 1;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA for chunk kb has landed
-    __builtin_amdgcn_s_barrier();    // ... and every other wave's; stage^1 is free
-
-    const uint8_t* st = smem + stage * C::STAGE;
-    v8i af[C::FM], bfr[C::FN];
-    float sav[C::FM];
+  // Promotion of one chunk: the MFMA of block b is issued before the FMAs of
+  // block b-1, so the VALU works while the matrix core runs.
+  // The scale products sA*sB replace the activation scales of the set.
+  auto scales = [&](F& f) {
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j) {
-      const uint8_t* base = st + (a_row0 + 16 * j) * kKC;
-      const uint4 lo = *reinterpret_cast<const uint4*>(base + rd0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(base + rd1);
-      af[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      sav[j] = reinterpret_cast<const float*>(st + C::A_BYTES + C::B_BYTES)[a_row0 + 16 * j + fr];
-    }
-#pragma unroll
-    for (int i = 0; i < C::FN; ++i) {
-      const uint8_t* base = st + C::A_BYTES + (b_row0 + 16 * i) * kKC;
-      const uint4 lo = *reinterpret_cast<const uint4*>(base + rd0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(base + rd1);
-      bfr[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    const float sbv = reinterpret_cast<const float*>(st + C::A_BYTES + C::B_BYTES + C::SA_BYTES)[sb_idx];
-
-    if (kb + 1 < KT) issue(kb + 1, stage ^ 1);
-
-    float sc[C::FM];
-#pragma unroll
-    for (int j = 0; j < C::FM; ++j) sc[j] = sav[j] * sbv;
-
-    // Software pipeline: the MFMA of block b is issued before the promotion
-    // FMAs of block b-1, so the VALU works while the matrix core runs.
-    constexpr int NBLK = C::FN * C::FM;
+    for (int j = 0; j < C::FM; ++j) f.sa[j] = f.sa[j] * f.sb;
+  };
+  // Blocks (i0 + i, j) for the FNH weight fragments held in f.
+  auto compute = [&](const F& f, int i0) {
+    const float* sc = f.sa;
+    constexpr int NBLK = FNH * C::FM;
     const v4f pz = {0.f, 0.f, 0.f, 0.f};
     v4f pc[2];
-    pc[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[0], af[0], pz, 0, 0, 0, 0, 0, 0);
+    pc[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[0], f.a[0], pz, 0, 0, 0, 0, 0, 0);
 #pragma unroll
     for (int b = 1; b <= NBLK; ++b) {
       if (b < NBLK)
-        pc[b & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[b / C::FM], af[b % C::FM], pz,
+        pc[b & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[b / C::FM], f.a[b % C::FM], pz,
                                                                      0, 0, 0, 0, 0, 0);
       const int pb = b - 1;
-      v4f& ac = acc[pb / C::FM][pb % C::FM];
+      v4f& ac = acc[i0 + pb / C::FM][pb % C::FM];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ac[r] = __builtin_fmaf(pc[pb & 1][r], sc[pb % C::FM], ac[r]);
     }
+    // Keep that order through scheduling: the first MFMA, then each further
+    // MFMA followed by the four FMAs of the block before it, then the last
+    // block's FMAs.
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+    for (int b = 1; b < NBLK; ++b) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  };
+
+  // ---- main loop ----------------------------------------------------------
+  // Every step is straight-line code (one basic block), so the scheduling
+  // barriers hold and no step needs more registers than another.  A step
+  // waits for this wave's outstanding LDS reads and DMA, meets the other
+  // waves at the barrier (so every wave's DMA has landed and every wave is
+  // done reading the stage the next DMA overwrites), starts that DMA, then
+  // reads fragments and computes.  Past the last chunk the DMA goes through
+  // the zero-record descriptor and reads touch a stale stage.
+  if constexpr (C::DB) {
+    // Two fragment sets: chunk kb's fragments were read in the previous
+    // step; read chunk kb+1's while computing chunk kb.
+    F f0, f1;
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    issue(1, 1);
+    read_a(0, f0);
+    read_b(0, f0, 0);
+    auto step = [&](int kb, F& cur, F& nxt, int stage) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_lgkm0<0>();   // chunk kb+1's DMA has landed
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kb + 2, stage);
+      read_a(stage ^ 1, nxt);
+      read_b(stage ^ 1, nxt, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      scales(cur);
+      compute(cur, 0);
+    };
+    int kb = 0;
+    for (; kb + 1 < KT; kb += 2) {
+      step(kb, f0, f1, 0);
+      step(kb + 1, f1, f0, 1);
+    }
+    if (kb < KT) step(kb, f0, f1, 0);
+  } else {
+    // One fragment set holding the activation fragments and half of the
+    // weight fragments: the second half is read once the first half's MFMAs
+    // have been issued.
+    F f;
+    issue(0, 0);
+    auto step = [&](int kb, int stage) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_lgkm0<0>();   // chunk kb's DMA has landed
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kb + 1, stage ^ 1);
+      read_a(stage, f);
+      read_b(stage, f, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      scales(f);
+      compute(f, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(stage, f, FNH);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f, FNH);
+    };
+    int kb = 0;
+    for (; kb + 1 < KT; kb += 2) {
+      step(kb, 0);
+      step(kb + 1, 1);
+    }
+    if (kb < KT) step(kb, 0);
   }
+  __builtin_amdgcn_s_waitcnt(0);   // no LDS write may still be in flight at exit
 
   // ---- epilogue: lane holds D[m][n .. n+3] per fragment ------------------
 #pragma unroll
@@ -264,32 +462,45 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs p) {
       }
     }
   }
+#endif
 }
 
-template <int BM, int BN, int MODE>
+template <class C, int MODE>
 hipError_t launch_cfg(const GemmProblem& pr, hipStream_t stream) {
   GemmArgs a;
   a.a = pr.a; a.sa = pr.sa; a.b = pr.b; a.sb = pr.sb; a.d = pr.d; a.groups = pr.groups;
   a.M = pr.M; a.N = pr.N; a.K = pr.K; a.G = pr.G;
-  a.tiles_m = (int32_t)((pr.M + BM - 1) / BM);
-  a.tiles_n = (int32_t)((pr.N + BN - 1) / BN);
+  a.tiles_m = (int32_t)((pr.M + C::BM - 1) / C::BM);
+  if (MODE == kContiguous) a.tiles_m = (int32_t)(pr.M / C::BM + pr.G);   // per-group tiles, upper bound
+  a.tiles_n = (int32_t)((pr.N + C::BN - 1) / C::BN);
   a.group_m = 8;
-  int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * (MODE == kMasked ? pr.G : 1);
+  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * (MODE == kMasked ? pr.G : 1);
   if (blocks == 0) return hipSuccess;
   if (pr.out_f32)
-    hipLaunchKernelGGL((k_gemm<BM, BN, MODE, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_gemm<C, MODE, true>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_gemm<BM, BN, MODE, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_gemm<C, MODE, false>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
   return hipGetLastError();
+}
+
+// Tile choice.  The 256x256 tile needs about half the operand traffic per
+// MFMA of the 128x128 one, but it only pays off when there are enough tiles
+// to fill the 256 CUs.
+template <int MODE>
+hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
+  const int64_t rows = (MODE == kMasked) ? p.M * p.G : p.M;
+  const int64_t large_tiles = ((rows + 255) / 256) * ((p.N + 255) / 256);
+  if (large_tiles >= 256) return launch_cfg<LargeTile, MODE>(p, stream);
+  return launch_cfg<SmallTile, MODE>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
   switch (p.mode) {
-    case kDense: return launch_cfg<128, 128, kDense>(p, stream);
-    case kContiguous: return launch_cfg<128, 128, kContiguous>(p, stream);
-    default: return launch_cfg<128, 128, kMasked>(p, stream);
+    case kDense: return dispatch<kDense>(p, stream);
+    case kContiguous: return dispatch<kContiguous>(p, stream);
+    default: return dispatch<kMasked>(p, stream);
   }
 }
 
