@@ -13,8 +13,8 @@ before the timed region.
 Printed as one JSON line, with
   roofline      the GEMM kernel alone, timed with HIP events on the stream it
                 runs on, against the MI355X dense FP8 MFMA peak (5.0 PFLOP/s);
-  cpu_baseline  the CPU oracle (NumPy, float64) timed on this host on a
-                256-row slice of the same workload;
+  cpu_baseline  the CPU oracle (NumPy, float64) timed on this host on the
+                same step, twice;
   kernels       every kernel of the hot path on its own workload (1x128 and
                 transpose quantizers on 8192 x 7168, the decode-shaped GEMM
                 128 x 24576 x 1536 with its quantizer, the MoE contiguous and
@@ -37,6 +37,10 @@ sys.path.insert(0, ROOT)
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 WORKLOAD = dict(name="dense_4096x2112x7168", M=4096, N=2112, K=7168)
+# rocprofv3 summary of the dominant kernel on this workload, and the sources it was built from
+GEMM_PROFILE = "profiles/k_gemm_dense_4096x2112x7168.md"
+GEMM_SOURCES = ["fp8_block_scaled_04_amd/csrc/gemm.hip", "fp8_block_scaled_04_amd/csrc/device_common.h",
+                "fp8_block_scaled_04_amd/csrc/launch.h"]
 
 
 def dev_bf16(bits):
@@ -136,25 +140,47 @@ def extra_kernels(fb, synth):
     return out
 
 
-def cpu_baseline(synth):
-    """The CPU oracle on a 256-row slice of the workload (1x128 quantization of
-    the slice + its GEMM against the full weight), in TFLOP/s of GEMM work."""
+def cpu_baseline(synth, reps=2):
+    """The CPU oracle on the same step: 1x128 quantization of the whole BF16
+    activation and its GEMM against the quantized weight, run `reps` times,
+    in TFLOP/s of GEMM work per step."""
     from oracle import gemm as og, quantize as oq
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    M, N, K = 256, WORKLOAD["N"], WORKLOAD["K"]
-    w = synth.dense(WORKLOAD["M"], N, K, seed=0)
+    M, N, K = WORKLOAD["M"], WORKLOAD["N"], WORKLOAD["K"]
+    w = synth.dense(M, N, K, seed=0)
     bq, bs = oq.quantize_128x128(w["b"])
     t0 = time.perf_counter()
-    a, sa = oq.quantize_1x128(w["a"][:M])
-    _ = og.gemm_ref(a, sa, bq, bs, "bf16")
-    dt = time.perf_counter() - t0
+    for _ in range(reps):
+        a, sa = oq.quantize_1x128(w["a"])
+        _ = og.gemm_ref(a, sa, bq, bs, "bf16")
+    dt = (time.perf_counter() - t0) / reps
     return dict(value=2 * M * N * K / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"rows 0..255 of A (256x{K}) quantized 1x128 and multiplied by the full "
-                       f"{N}x{K} weight: {2 * M * N * K / 1e9:.2f} GFLOP in {dt:.2f} s")
+                sample=f"the whole step ({M}x{K} activation quantized 1x128, then its {M}x{N}x{K} GEMM, "
+                       f"{2 * M * N * K / 1e9:.0f} GFLOP) run {reps} times: {dt:.2f} s per step")
+
+
+def profile_traffic(path, sources):
+    """HBM-side bytes per launch of the dominant kernel, as recorded in a
+    rocprofv3 summary under profiles/, or None when the kernel's sources have
+    changed since the counters were taken (the summary stores their hash)."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, path)).read()
+    except OSError:
+        return None
+    tb = [l.split(":", 1)[1].strip() for l in text.splitlines() if l.startswith("traffic_bytes_per_launch:")]
+    hs = [l.split(":", 1)[1].split()[0] for l in text.splitlines() if l.startswith("kernel_source_sha256_16:")]
+    if not tb or not hs:
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return int(tb[0]) if h.hexdigest()[:16] == hs[0] else None
 
 
 def main():
@@ -164,11 +190,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel workload table")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a single "
-              "device; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "device: each kernel works on one GPU's share and nothing here communicates)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibrate:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": 5}), flush=True)
+        return
 
     from fp8_block_scaled_04_amd import fp8bs as fb, synth
 
@@ -220,7 +258,8 @@ def main():
         "config": {"workload": "fp8 linear forward: quantize_1x128(A bf16 4096x7168) + block-scaled GEMM "
                                "4096x2112x7168, bf16 out", "M": M, "N": N, "K": K},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved / FP8_PEAK_TFLOPS,
+                     "traffic": profile_traffic(GEMM_PROFILE, GEMM_SOURCES),
                      "kernel": "k_gemm (dense)", "kernel_us": gemm_us},
     }
     if not args.no_extra:
