@@ -140,17 +140,18 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X
 // (workgroup i runs on XCD i % 8).  Renumber them so that consecutive logical
 // ids land on the same XCD, which keeps tiles that share operand panels in one
-// L2.  Valid for any total: the first `total % 8` XCDs get one extra id.
+// L2, and so that every XCD gets an equal share of the `total` ids that have
+// work: XCD x takes total/8 ids (one more for x < total % 8).  `total` may be
+// below the grid size (grids sized for the worst case); workgroups beyond
+// their XCD's share get -1 and have nothing to do.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int xcd_remap(int pid, int total) {
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
   constexpr int kXcds = 8;
-  int per = (total + kXcds - 1) / kXcds;
-  int tall = total % kXcds;
-  if (tall == 0) tall = kXcds;
-  int xcd = pid % kXcds;
-  int local = pid / kXcds;
-  return (xcd < tall) ? xcd * per + local
-                      : tall * per + (xcd - tall) * (per - 1) + local;
+  const int q = total / kXcds, r = total % kXcds;
+  const int xcd = bid % kXcds, local = bid / kXcds;
+  const int share = q + (xcd < r ? 1 : 0);
+  if (local >= share) return -1;
+  return xcd * q + min(xcd, r) + local;
 }
 
 }  // namespace fp8bs

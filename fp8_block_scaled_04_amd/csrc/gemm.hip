@@ -95,7 +95,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // readfirstlane'd fields so it lives in SGPRs.
 __device__ __forceinline__ v4i make_rsrc(const void* base, int64_t bytes) {
   const uint64_t a = (uint64_t)base;
-  const int64_t nb = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes;
+  const int64_t nb = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : bytes);
   v4i r;
   r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
@@ -142,6 +142,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p);
 }
 
+// Valid rows of a masked group: the device-side count clamped to [0, cap].
+__device__ __forceinline__ int64_t masked_count(int32_t c, int64_t cap) {
+  return c < 0 ? 0 : (c > cap ? cap : (int64_t)c);
+}
+// Rows [lo, hi) of contiguous group g, clamped into [0, Mt] so that any
+// offsets array keeps every access inside the buffers.
+__device__ __forceinline__ void group_rows(const int32_t* offs, int g, int64_t mt, int64_t& lo, int64_t& hi) {
+  lo = offs[g];
+  hi = offs[g + 1];
+  lo = lo < 0 ? 0 : (lo > mt ? mt : lo);
+  hi = hi < lo ? lo : (hi > mt ? mt : hi);
+}
+
 struct GemmArgs {
   const uint8_t* a;
   const float* sa;
@@ -151,7 +164,7 @@ struct GemmArgs {
   const int32_t* groups;
   int64_t M, N, K;
   int32_t G;
-  int32_t tiles_m, tiles_n;   // tile grid (contiguous: Mt/BM + G virtual m-tiles)
+  int32_t tiles_m, tiles_n;   // dense: tile grid; grouped: per-group / worst-case bound
   int32_t group_m;
 };
 
@@ -179,27 +192,9 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   const int64_t NB = (N + 127) / 128;
 
   // ---- tile -> (group, rows, columns) ------------------------------------
-  const int total = (int)gridDim.x;
-  const int pid = xcd_remap((int)blockIdx.x, total);
-  int g = 0, tm, tn;
-  if (MODE == kMasked) {
-    const int per_g = p.tiles_m * p.tiles_n;
-    g = pid / per_g;
-    const int r = pid - g * per_g;
-    tn = r / p.tiles_m;
-    tm = r - tn * p.tiles_m;
-  } else {
-    const int width = p.group_m * p.tiles_n;
-    const int grp = pid / width;
-    const int first_m = grp * p.group_m;
-    const int gsz = min(p.tiles_m - first_m, p.group_m);
-    const int r = pid - grp * width;
-    tm = first_m + r % gsz;
-    tn = r / gsz;
-  }
-  const int64_t n0 = (int64_t)tn * BN;
-  int64_t m0 = (int64_t)tm * BM;
-
+  // The grouped layouts launch a grid sized for the worst case; the tiles
+  // that exist are counted here from the device-side group sizes, numbered
+  // 0 .. total-1, and spread evenly over the XCDs.
   const uint8_t* a_base = p.a;
   const float* sa_base = p.sa;
   const uint8_t* b_base = p.b;
@@ -208,38 +203,73 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   int64_t m_valid = p.M;           // rows that are computed and stored
   const int64_t sa_stride = p.M;   // distance between consecutive K chunks in sA
   int64_t d_row0 = 0;              // first output row of this group's block of D
-  if (MODE == kContiguous) {
-    // Tiles are laid out per group (group boundaries are only multiples of
-    // 128): virtual m-tile tm is tile t of group g, where tm = (tile counts
-    // of the groups before g) + t.
-    const int32_t* offs = p.groups;
-    int first = 0;
-    bool found = false;
-    for (int gg = 0; gg < p.G; ++gg) {
-      const int64_t lo = offs[gg], hi = offs[gg + 1];
-      const int cnt = (int)((hi - lo + BM - 1) / BM);
-      if (tm < first + cnt) {
-        g = gg;
-        m0 = lo + (int64_t)(tm - first) * BM;
-        m_valid = hi;
-        found = true;
-        break;
-      }
-      first += cnt;
+  int64_t m0, n0;
+  if (MODE == kMasked) {
+    // Tiles in group order; within a group, m fastest.
+    int total = 0;
+    for (int gg = 0; gg < p.G; ++gg) total += (int)((masked_count(p.groups[gg], p.M) + BM - 1) / BM);
+    total *= p.tiles_n;
+    int pid = xcd_remap((int)blockIdx.x, total);
+    if (pid < 0) return;
+    int g = 0, cnt = 0;
+    int64_t rows = 0;
+    for (; g < p.G; ++g) {
+      rows = masked_count(p.groups[g], p.M);
+      cnt = (int)((rows + BM - 1) / BM) * p.tiles_n;
+      if (pid < cnt) break;
+      pid -= cnt;
     }
-    if (!found) return;
-    b_base += (int64_t)g * N * K;
-    sb_base += (int64_t)g * NB * KT;
-  } else if (MODE == kMasked) {
-    int64_t cnt = p.groups[g];
-    cnt = cnt < 0 ? 0 : (cnt > p.M ? p.M : cnt);
-    if (m0 >= cnt) return;
-    m_valid = cnt;
+    const int tcnt = cnt / p.tiles_n;
+    const int tn = pid / tcnt, tm = pid - tn * tcnt;
+    m0 = (int64_t)tm * BM;
+    n0 = (int64_t)tn * BN;
+    m_valid = rows;
     a_base += (int64_t)g * p.M * K;
     sa_base += (int64_t)g * KT * p.M;
     b_base += (int64_t)g * N * K;
     sb_base += (int64_t)g * NB * KT;
     d_row0 = (int64_t)g * p.M;
+  } else {
+    // Dense: the grid is exact.  Contiguous: tile t of group g has index
+    // (tiles of the groups before g) + t (group boundaries are multiples of
+    // 128 rows, so a tile never spans two groups).
+    int tiles_m = p.tiles_m;
+    if (MODE == kContiguous) {
+      tiles_m = 0;
+      for (int gg = 0; gg < p.G; ++gg) {
+        int64_t lo, hi;
+        group_rows(p.groups, gg, p.M, lo, hi);
+        tiles_m += (int)((hi - lo + BM - 1) / BM);
+      }
+    }
+    const int pid = xcd_remap((int)blockIdx.x, tiles_m * p.tiles_n);
+    if (pid < 0) return;
+    // Walk the tiles in groups of group_m tile rows, column by column.
+    const int width = p.group_m * p.tiles_n;
+    const int grp = pid / width;
+    const int first_m = grp * p.group_m;
+    const int gsz = min(tiles_m - first_m, p.group_m);
+    const int r = pid - grp * width;
+    int tm = first_m + r % gsz;
+    const int tn = r / gsz;
+    n0 = (int64_t)tn * BN;
+    m0 = (int64_t)tm * BM;
+    if (MODE == kContiguous) {
+      int g = 0;
+      for (; g < p.G; ++g) {
+        int64_t lo, hi;
+        group_rows(p.groups, g, p.M, lo, hi);
+        const int cnt = (int)((hi - lo + BM - 1) / BM);
+        if (tm < cnt) {
+          m0 = lo + (int64_t)tm * BM;
+          m_valid = hi;
+          break;
+        }
+        tm -= cnt;
+      }
+      b_base += (int64_t)g * N * K;
+      sb_base += (int64_t)g * NB * KT;
+    }
   }
 
   // ---- buffer resources (SGPRs) and per-lane DMA offsets ------------------
@@ -471,7 +501,9 @@ hipError_t launch_cfg(const GemmProblem& pr, hipStream_t stream) {
   a.a = pr.a; a.sa = pr.sa; a.b = pr.b; a.sb = pr.sb; a.d = pr.d; a.groups = pr.groups;
   a.M = pr.M; a.N = pr.N; a.K = pr.K; a.G = pr.G;
   a.tiles_m = (int32_t)((pr.M + C::BM - 1) / C::BM);
-  if (MODE == kContiguous) a.tiles_m = (int32_t)(pr.M / C::BM + pr.G);   // per-group tiles, upper bound
+  // Contiguous: every group may end in a partial tile, so at most Mt/BM + G
+  // tiles exist (the kernel counts the real ones from the offsets).
+  if (MODE == kContiguous) a.tiles_m = (int32_t)(pr.M / C::BM + pr.G);
   a.tiles_n = (int32_t)((pr.N + C::BN - 1) / C::BN);
   a.group_m = 8;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * (MODE == kMasked ? pr.G : 1);

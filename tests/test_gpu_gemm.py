@@ -36,7 +36,9 @@ def run(a, sa, b, sb, out_dtype=torch.bfloat16):
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (1, 16, 128), (37, 48, 384), (130, 2112, 256),
-                                   (256, 272, 1024), (64, 4096, 128), (300, 400, 640), (513, 144, 1152)])
+                                   (256, 272, 1024), (64, 4096, 128), (300, 400, 640), (513, 144, 1152),
+                                   # enough 256x256 tiles for the large-tile path; ragged edges
+                                   (4096, 4096, 256), (4000, 4112, 384)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_gemm_workload_recipe(M, N, K, out_dtype):
     print(f"gemm M={M} N={N} K={K} out={out_dtype}", flush=True)

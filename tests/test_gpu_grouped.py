@@ -47,6 +47,8 @@ def run_contiguous(a, sa, b, sb, offs, Mt, N):
     (3, 384, 2112, 128, [0, 128, 256, 384]),
     (5, 1024, 48, 640, None),                        # seeded multinomial sizes
     (2, 256, 16, 384, [0, 0, 0]),                    # every group empty
+    # large-tile path: 128-row groups end in half tiles, one group is empty
+    (7, 4608, 4096, 256, [0, 128, 128, 1152, 2304, 2432, 3840, 4480]),
 ])
 def test_contiguous(G, Mt, N, K, offsets):
     print(f"contiguous G={G} Mt={Mt} N={N} K={K} offs={offsets}", flush=True)
@@ -116,6 +118,8 @@ def run_masked(a, sa, b, sb, cnt, out_dtype=torch.bfloat16):
     (4, 256, 2112, 128, [1, 128, 129, 255]),
     (2, 64, 16, 512, [70, -3]),                      # counts outside [0, cap] are clamped
     (6, 256, 96, 640, None),                         # seeded uniform counts
+    # large-tile path (20 experts x 16 column tiles)
+    (20, 256, 4096, 256, [0, 1, 255, 256, 129, 128, 0, 7, 200, 256, 64, 3, 0, 0, 250, 100, 31, 256, 17, 90]),
 ])
 def test_masked(G, cap, N, K, counts):
     print(f"masked G={G} cap={cap} N={N} K={K} counts={counts}", flush=True)
