@@ -443,26 +443,129 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     }
     if (kb < KT) step(kb, f0, f1, 0);
   } else {
-    // One fragment set holding the activation fragments and half of the
-    // weight fragments: the second half is read once the first half's MFMAs
-    // have been issued.
+    // The activation fragments and the scales are read for the whole chunk;
+    // the weight fragments rotate through FNH register slots, each read two
+    // rows of MFMAs (2*FM blocks) before its first use, so the LDS reads of a
+    // step overlap its MFMAs instead of preceding them.
+    static_assert(FNH >= 4, "the weight ring reads two rows ahead");
     F f;
+    auto read_a1 = [&](int stage, int j) {
+      const uint8_t* base = smem + stage * C::STAGE + (a_row0 + 16 * j) * kKC;
+      const uint4 lo = *reinterpret_cast<const uint4*>(base + rd0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(base + rd1);
+      f.a[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    auto read_b1 = [&](int stage, int i) {
+      const uint8_t* base = smem + stage * C::STAGE + C::A_BYTES + (b_row0 + 16 * i) * kKC;
+      const uint4 lo = *reinterpret_cast<const uint4*>(base + rd0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(base + rd1);
+      f.b[i % FNH] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    auto read_sc = [&](int stage) {
+      const uint8_t* st = smem + stage * C::STAGE;
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) f.sa[j] = reinterpret_cast<const float*>(st + C::SA_OFF)[a_row0 + 16 * j + fr];
+      f.sb = reinterpret_cast<const float*>(st + C::SB_OFF)[sb_idx];
+    };
+    // Blocks b = i*FM + j (weight fragment i, activation fragment j).
+    constexpr int NBLK = C::FN * C::FM;
+    constexpr int LAST = NBLK - C::FM;   // first block of the last row
+    const v4f pz = {0.f, 0.f, 0.f, 0.f};
+    v4f pc[2];
+    auto mfma = [&](int b) {
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[(b / C::FM) % FNH], f.a[b % C::FM], pz,
+                                                              0, 0, 0, 0, 0, 0);
+    };
+    auto fma_block = [&](int b, const v4f& pv, const float* sc) {
+      v4f& ac = acc[b / C::FM][b % C::FM];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ac[r] = __builtin_fmaf(pv[r], sc[b % C::FM], ac[r]);
+    };
+    // Rows 0 .. FN-2; weight fragment i+2 is read at the start of row i.
+    auto rows = [&](int stage) {
+      pc[0] = mfma(0);
+      read_b1(stage, 2);
+#pragma unroll
+      for (int b = 1; b < LAST; ++b) {
+        pc[b & 1] = mfma(b);
+        if (b % C::FM == 0 && b / C::FM + 2 < C::FN) read_b1(stage, b / C::FM + 2);
+        fma_block(b - 1, pc[(b - 1) & 1], f.sa);
+      }
+      // Order: MFMA, [weight read at the start of a row], the FMAs of the
+      // previous block.
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int b = 1; b < LAST; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (b % C::FM == 0 && b / C::FM + 2 < C::FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    };
+    // The last row.  Each MFMA frees its activation fragment, which is then
+    // refilled with the next chunk's (from stage nstage); weight fragments 0
+    // and 1 and the scales of the next chunk follow.  The FMAs keep this
+    // chunk's scales.
+    auto last_row = [&](int nstage) {
+      float sc[C::FM];
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) sc[j] = f.sa[j];
+#pragma unroll
+      for (int b = LAST; b <= NBLK; ++b) {
+        if (b < NBLK) {
+          const int j = b % C::FM;
+          pc[b & 1] = mfma(b);
+          read_a1(nstage, j);
+          if (j == 0) read_b1(nstage, 0);
+          if (j == 0) read_sc(nstage);
+          if (j == 1) read_b1(nstage, 1);
+        }
+        fma_block(b - 1, pc[(b - 1) & 1], sc);
+      }
+      // Order: MFMA, the reads of the next chunk it makes room for, the FMAs
+      // of the previous block.
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+      for (int j = 2; j < C::FM; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    };
+    // Prologue: chunk 0 in stage 0, chunk 1 on its way to stage 1, chunk 0's
+    // first fragments read.
     issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    issue(1, 1);
+    read_a1(0, 0);
+    read_b1(0, 0);
+    read_sc(0);
+#pragma unroll
+    for (int j = 1; j < C::FM; ++j) read_a1(0, j);
+    read_b1(0, 1);
+    // Step kb (chunk kb in stage `stage`): rows 0 .. FN-2, then wait for
+    // chunk kb+1's DMA and meet the other waves (every wave now holds all of
+    // chunk kb in registers, so its stage is free), start chunk kb+2's DMA
+    // into it, and run the last row while reading chunk kb+1's first
+    // fragments.
     auto step = [&](int kb, int stage) {
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm_lgkm0<0>();   // chunk kb's DMA has landed
+      scales(f);
+      rows(stage);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue(kb + 1, stage ^ 1);
-      read_a(stage, f);
-      read_b(stage, f, 0);
+      issue(kb + 2, stage);
       __builtin_amdgcn_sched_barrier(0);
-      scales(f);
-      compute(f, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      read_b(stage, f, FNH);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(f, FNH);
+      last_row(stage ^ 1);
     };
     int kb = 0;
     for (; kb + 1 < KT; kb += 2) {
