@@ -506,27 +506,39 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     // refilled with the next chunk's (from stage nstage); weight fragments 0
     // and 1 and the scales of the next chunk follow.  The FMAs keep this
     // chunk's scales.
-    auto last_row = [&](int nstage) {
+    // The last row.  Each MFMA frees its activation fragment, which is then
+    // refilled with the next chunk's (from stage nstage); weight fragments 0
+    // and 1 and the scales of the next chunk follow.  The FMAs keep this
+    // chunk's scales.  `mid` (the next DMA) is issued once the first MFMA of
+    // the row is running, so the matrix core restarts right after the
+    // barrier.
+    auto last_row = [&](int nstage, auto&& mid) {
       float sc[C::FM];
 #pragma unroll
       for (int j = 0; j < C::FM; ++j) sc[j] = f.sa[j];
+      pc[LAST & 1] = mfma(LAST);
+      read_a1(nstage, 0);
+      read_b1(nstage, 0);
+      read_sc(nstage);
+      fma_block(LAST - 1, pc[(LAST - 1) & 1], sc);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mid();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = LAST; b <= NBLK; ++b) {
+      for (int b = LAST + 1; b <= NBLK; ++b) {
         if (b < NBLK) {
           const int j = b % C::FM;
           pc[b & 1] = mfma(b);
           read_a1(nstage, j);
-          if (j == 0) read_b1(nstage, 0);
-          if (j == 0) read_sc(nstage);
           if (j == 1) read_b1(nstage, 1);
         }
         fma_block(b - 1, pc[(b - 1) & 1], sc);
       }
       // Order: MFMA, the reads of the next chunk it makes room for, the FMAs
       // of the previous block.
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
@@ -552,9 +564,9 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     read_b1(0, 1);
     // Step kb (chunk kb in stage `stage`): rows 0 .. FN-2, then wait for
     // chunk kb+1's DMA and meet the other waves (every wave now holds all of
-    // chunk kb in registers, so its stage is free), start chunk kb+2's DMA
-    // into it, and run the last row while reading chunk kb+1's first
-    // fragments.
+    // chunk kb in registers, so its stage is free), and run the last row
+    // while reading chunk kb+1's first fragments and starting chunk kb+2's
+    // DMA into the freed stage.
     auto step = [&](int kb, int stage) {
       __builtin_amdgcn_sched_barrier(0);
       scales(f);
@@ -563,9 +575,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue(kb + 2, stage);
-      __builtin_amdgcn_sched_barrier(0);
-      last_row(stage ^ 1);
+      last_row(stage ^ 1, [&] { issue(kb + 2, stage); });
     };
     int kb = 0;
     for (; kb + 1 < KT; kb += 2) {
