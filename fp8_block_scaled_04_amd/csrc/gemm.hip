@@ -502,53 +502,53 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
     };
-    // The last row.  Each MFMA frees its activation fragment, which is then
-    // refilled with the next chunk's (from stage nstage); weight fragments 0
-    // and 1 and the scales of the next chunk follow.  The FMAs keep this
-    // chunk's scales.
-    // The last row.  Each MFMA frees its activation fragment, which is then
-    // refilled with the next chunk's (from stage nstage); weight fragments 0
-    // and 1 and the scales of the next chunk follow.  The FMAs keep this
-    // chunk's scales.  `mid` (the next DMA) is issued once the first MFMA of
-    // the row is running, so the matrix core restarts right after the
-    // barrier.
-    auto last_row = [&](int nstage, auto&& mid) {
+    // The last row, split around the synchronisation: its first two MFMAs
+    // (which need only this chunk's fragments) are issued before the wave
+    // waits at the barrier, so the matrix core has work queued while the
+    // waves meet.  After the barrier, each MFMA frees its activation
+    // fragment, which is refilled with the next chunk's (from stage nstage);
+    // weight fragments 0 and 1 and the next chunk's scales follow, and
+    // `sync` (wait + barrier) and `mid` (the next DMA) run in between.  The
+    // FMAs keep this chunk's scales.
+    static_assert(C::FM == 4, "the last row is written for four activation fragments");
+    auto last_row = [&](int nstage, auto&& sync, auto&& mid) {
       float sc[C::FM];
 #pragma unroll
       for (int j = 0; j < C::FM; ++j) sc[j] = f.sa[j];
       pc[LAST & 1] = mfma(LAST);
+      fma_block(LAST - 1, pc[(LAST - 1) & 1], sc);
+      pc[(LAST + 1) & 1] = mfma(LAST + 1);
+      fma_block(LAST, pc[LAST & 1], sc);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      sync();
+      __builtin_amdgcn_sched_barrier(0);
       read_a1(nstage, 0);
       read_b1(nstage, 0);
+      __builtin_amdgcn_sched_barrier(0);
       read_sc(nstage);
-      fma_block(LAST - 1, pc[(LAST - 1) & 1], sc);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_a1(nstage, 1);
+      read_b1(nstage, 1);
       __builtin_amdgcn_sched_barrier(0);
       mid();
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int b = LAST + 1; b <= NBLK; ++b) {
-        if (b < NBLK) {
-          const int j = b % C::FM;
-          pc[b & 1] = mfma(b);
-          read_a1(nstage, j);
-          if (j == 1) read_b1(nstage, 1);
-        }
-        fma_block(b - 1, pc[(b - 1) & 1], sc);
-      }
-      // Order: MFMA, the reads of the next chunk it makes room for, the FMAs
-      // of the previous block.
+      pc[(LAST + 2) & 1] = mfma(LAST + 2);
+      read_a1(nstage, 2);
+      fma_block(LAST + 1, pc[(LAST + 1) & 1], sc);
+      pc[(LAST + 3) & 1] = mfma(LAST + 3);
+      read_a1(nstage, 3);
+      fma_block(LAST + 2, pc[(LAST + 2) & 1], sc);
+      fma_block(LAST + 3, pc[(LAST + 3) & 1], sc);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-#pragma unroll
-      for (int j = 2; j < C::FM; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     };
     // Prologue: chunk 0 in stage 0, chunk 1 on its way to stage 1, chunk 0's
     // first fragments read.
@@ -562,20 +562,22 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
 #pragma unroll
     for (int j = 1; j < C::FM; ++j) read_a1(0, j);
     read_b1(0, 1);
-    // Step kb (chunk kb in stage `stage`): rows 0 .. FN-2, then wait for
-    // chunk kb+1's DMA and meet the other waves (every wave now holds all of
-    // chunk kb in registers, so its stage is free), and run the last row
-    // while reading chunk kb+1's first fragments and starting chunk kb+2's
+    // Step kb (chunk kb in stage `stage`): rows 0 .. FN-2, then the last row,
+    // inside which the wave waits for chunk kb+1's DMA and meets the other
+    // waves (every wave then holds all of chunk kb in registers, so its stage
+    // is free), reads chunk kb+1's first fragments and starts chunk kb+2's
     // DMA into the freed stage.
     auto step = [&](int kb, int stage) {
       __builtin_amdgcn_sched_barrier(0);
       scales(f);
       rows(stage);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm_lgkm0<0>();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      last_row(stage ^ 1, [&] { issue(kb + 2, stage); });
+      last_row(stage ^ 1,
+               [&] {
+                 wait_vm_lgkm0<0>();
+                 __builtin_amdgcn_s_barrier();
+               },
+               [&] { issue(kb + 2, stage); });
     };
     int kb = 0;
     for (; kb + 1 < KT; kb += 2) {
