@@ -64,17 +64,25 @@ struct Cfg {
   static constexpr int SA_OFF = A_BYTES + B_BYTES;
   static constexpr int SB_OFF = A_BYTES + B_BYTES + SA_WAVES * 256;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE;
   static constexpr int A_LOADS = BM / (8 * NW);     // 8 rows of 128 bytes per wave instruction
-  static constexpr int B_LOADS = BN / (8 * NW);
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "rows must split evenly over the waves");
+  static constexpr int B_LOADS = (BN + 8 * NW - 1) / (8 * NW);
+  // When BN rows do not split evenly over the waves, the waves past the end
+  // in the last B instruction load nothing (zero-size descriptor) into a
+  // scratch kilobyte of LDS after the two stages.
+  static constexpr bool B_TAIL = BN % (8 * NW) != 0;
+  static constexpr int JUNK_OFF = 2 * STAGE;
+  static constexpr int LDS_BYTES = 2 * STAGE + (B_TAIL ? 1024 : 0);
+  static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES;
+  static_assert(BM % (8 * NW) == 0 && BN % 16 == 0, "A rows split evenly over the waves; B rows are fragments");
   static_assert(SA_WAVES < NW, "one wave must be left for the weight scales");
-  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-row weight block");
+  static_assert(WN % 16 == 0 && WN <= 128, "a wave's columns are whole fragments within at most two weight blocks");
+  static_assert(DB_ == false || 128 % WN == 0, "the double-buffered path needs a wave's columns in one weight block");
   static_assert(LDS_BYTES <= 160 * 1024, "two stages must fit in LDS");
 };
 
 using SmallTile = Cfg<128, 128, 2, 2, true>;
 using LargeTile = Cfg<256, 256, 4, 2, false>;
+using MidTile = Cfg<256, 160, 4, 2, false>;
 
 // LDS layout of an operand chunk: rows of 128 bytes (one K chunk), row-major,
 // with the 16-byte segments of row r XOR-swizzled: logical segment s is
@@ -324,8 +332,16 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     for (int i = 0; i < C::A_LOADS; ++i)
       dma16(rak, st + (i * C::NW + wave) * 8 * kKC, ro + i * row_step, koff);
 #pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i)
-      dma16(rbk, st + C::A_BYTES + (i * C::NW + wave) * 8 * kKC, ro + i * row_step, koff);
+    for (int i = 0; i < C::B_LOADS; ++i) {
+      const int r0 = (i * C::NW + wave) * 8;   // first of the 8 rows of this instruction
+      if (C::B_TAIL && i == C::B_LOADS - 1) {
+        const bool act = r0 < BN;
+        dma16(act ? rbk : r_none, act ? st + C::A_BYTES + r0 * kKC : smem_lds + C::JUNK_OFF, ro + i * row_step,
+              koff);
+      } else {
+        dma16(rbk, st + C::A_BYTES + r0 * kKC, ro + i * row_step, koff);
+      }
+    }
     dma4(rck, st + C::SA_OFF + wave * 256, sc_voff, soff);
   };
   constexpr int DMA_PER_CHUNK = C::A_LOADS + C::B_LOADS + 1;   // vmcnt of one issue()
@@ -444,36 +460,61 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     if (kb < KT) step(kb, f0, f1, 0);
   } else {
     // The activation fragments and the scales are read for the whole chunk;
-    // the weight fragments rotate through FNH register slots, each read two
-    // rows of MFMAs (2*FM blocks) before its first use, so the LDS reads of a
-    // step overlap its MFMAs instead of preceding them.
-    static_assert(FNH >= 4, "the weight ring reads two rows ahead");
-    F f;
+    // the weight fragments rotate through a ring of register slots, each
+    // read two rows of MFMAs (2*FM blocks) before its first use, so the LDS
+    // reads of a step overlap its MFMAs instead of preceding them.  Slot of
+    // weight fragment i: i % 4, except that the last fragment gets a fifth
+    // slot when i % 4 would be slot 0 or 1, which the next chunk's first two
+    // fragments are read into during the last row.
+    static_assert(C::FM == 4, "the last row is written for four activation fragments");
+    constexpr int FN = C::FN;
+    constexpr bool EXTRA = (FN % 4 == 1) || (FN % 4 == 2);
+    constexpr int SLOTS = EXTRA ? 5 : 4;
+    auto slot = [](int i) { return (EXTRA && i == FN - 1) ? 4 : i % 4; };
+    // A wave's columns lie in one 128-row weight block when WN divides 128;
+    // otherwise (straddle) they may span two, and the weight scale is chosen
+    // per weight fragment.
+    constexpr bool STRADDLE = (128 % C::WN) != 0;
+    static_assert(C::WN <= 128, "a wave's columns span at most two weight blocks");
+    v8i fa[C::FM], fb[SLOTS];
+    float sa[C::FM];          // activation scales (times the weight scale unless STRADDLE)
+    float sb_lo = 0.f, sb_hi = 0.f;
+    const int blk_lo = sb_idx;
+    const int blk_hi = (int)((n0 + b_row0 + C::WN - 1) / 128 - n0 / 128);
     auto read_a1 = [&](int stage, int j) {
       const uint8_t* base = smem + stage * C::STAGE + (a_row0 + 16 * j) * kKC;
       const uint4 lo = *reinterpret_cast<const uint4*>(base + rd0);
       const uint4 hi = *reinterpret_cast<const uint4*>(base + rd1);
-      f.a[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      fa[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
     auto read_b1 = [&](int stage, int i) {
       const uint8_t* base = smem + stage * C::STAGE + C::A_BYTES + (b_row0 + 16 * i) * kKC;
       const uint4 lo = *reinterpret_cast<const uint4*>(base + rd0);
       const uint4 hi = *reinterpret_cast<const uint4*>(base + rd1);
-      f.b[i % FNH] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      fb[slot(i)] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
     auto read_sc = [&](int stage) {
       const uint8_t* st = smem + stage * C::STAGE;
 #pragma unroll
-      for (int j = 0; j < C::FM; ++j) f.sa[j] = reinterpret_cast<const float*>(st + C::SA_OFF)[a_row0 + 16 * j + fr];
-      f.sb = reinterpret_cast<const float*>(st + C::SB_OFF)[sb_idx];
+      for (int j = 0; j < C::FM; ++j) sa[j] = reinterpret_cast<const float*>(st + C::SA_OFF)[a_row0 + 16 * j + fr];
+      sb_lo = reinterpret_cast<const float*>(st + C::SB_OFF)[blk_lo];
+      if (STRADDLE) sb_hi = reinterpret_cast<const float*>(st + C::SB_OFF)[blk_hi];
+    };
+    // Scale products of weight fragment i: sa * sb(block of fragment i).
+    auto row_scales = [&](int i, float* sc) {
+      const bool hi_blk = (int)((n0 + b_row0 + 16 * i) / 128 - n0 / 128) != blk_lo;
+      const float sbi = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                            __builtin_bit_cast(int, hi_blk ? sb_hi : sb_lo)));
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) sc[j] = sa[j] * sbi;
     };
     // Blocks b = i*FM + j (weight fragment i, activation fragment j).
-    constexpr int NBLK = C::FN * C::FM;
+    constexpr int NBLK = FN * C::FM;
     constexpr int LAST = NBLK - C::FM;   // first block of the last row
     const v4f pz = {0.f, 0.f, 0.f, 0.f};
     v4f pc[2];
     auto mfma = [&](int b) {
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[(b / C::FM) % FNH], f.a[b % C::FM], pz,
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[slot(b / C::FM)], fa[b % C::FM], pz,
                                                               0, 0, 0, 0, 0, 0);
     };
     auto fma_block = [&](int b, const v4f& pv, const float* sc) {
@@ -482,24 +523,41 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       for (int r = 0; r < 4; ++r) ac[r] = __builtin_fmaf(pv[r], sc[b % C::FM], ac[r]);
     };
     // Rows 0 .. FN-2; weight fragment i+2 is read at the start of row i.
-    auto rows = [&](int stage) {
+    // Returns, in scl, the scale products of row FN-2 (its last block's FMAs
+    // run in the last row).
+    auto rows = [&](int stage, float* scl) {
+      float sc[2][C::FM];
+      if (STRADDLE) row_scales(0, sc[0]);
+      else
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) sc[0][j] = sa[j];
       pc[0] = mfma(0);
-      read_b1(stage, 2);
+      if (2 < FN) read_b1(stage, 2);
 #pragma unroll
       for (int b = 1; b < LAST; ++b) {
+        const int i = b / C::FM;
         pc[b & 1] = mfma(b);
-        if (b % C::FM == 0 && b / C::FM + 2 < C::FN) read_b1(stage, b / C::FM + 2);
-        fma_block(b - 1, pc[(b - 1) & 1], f.sa);
+        if (b % C::FM == 0) {
+          if (i + 2 < FN) read_b1(stage, i + 2);
+          if (STRADDLE) row_scales(i, sc[i & 1]);
+          else
+#pragma unroll
+            for (int j = 0; j < C::FM; ++j) sc[i & 1][j] = sa[j];
+        }
+        fma_block(b - 1, pc[(b - 1) & 1], sc[((b - 1) / C::FM) & 1]);
       }
-      // Order: MFMA, [weight read at the start of a row], the FMAs of the
-      // previous block.
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) scl[j] = sc[(FN - 2) & 1][j];
+      // Order: MFMA, [at the start of a row: the weight read], the FMAs of the
+      // previous block [and the row's scale products].
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (2 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
       for (int b = 1; b < LAST; ++b) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (b % C::FM == 0 && b / C::FM + 2 < C::FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        if (b % C::FM == 0 && b / C::FM + 2 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (STRADDLE && b % C::FM == 0) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
     };
     // The last row, split around the synchronisation: its first two MFMAs
@@ -510,17 +568,18 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     // weight fragments 0 and 1 and the next chunk's scales follow, and
     // `sync` (wait + barrier) and `mid` (the next DMA) run in between.  The
     // FMAs keep this chunk's scales.
-    static_assert(C::FM == 4, "the last row is written for four activation fragments");
-    auto last_row = [&](int nstage, auto&& sync, auto&& mid) {
+    auto last_row = [&](int nstage, const float* scp, auto&& sync, auto&& mid) {
       float sc[C::FM];
+      if (STRADDLE) row_scales(FN - 1, sc);
+      else
 #pragma unroll
-      for (int j = 0; j < C::FM; ++j) sc[j] = f.sa[j];
+        for (int j = 0; j < C::FM; ++j) sc[j] = sa[j];
       pc[LAST & 1] = mfma(LAST);
-      fma_block(LAST - 1, pc[(LAST - 1) & 1], sc);
+      fma_block(LAST - 1, pc[(LAST - 1) & 1], scp);
       pc[(LAST + 1) & 1] = mfma(LAST + 1);
       fma_block(LAST, pc[LAST & 1], sc);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, STRADDLE ? 8 : 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -550,6 +609,12 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     };
+    // Without straddling, every row uses sa * sb: multiply once per chunk.
+    auto chunk_scales = [&] {
+      if (!STRADDLE)
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) sa[j] = sa[j] * sb_lo;
+    };
     // Prologue: chunk 0 in stage 0, chunk 1 on its way to stage 1, chunk 0's
     // first fragments read.
     issue(0, 0);
@@ -569,10 +634,11 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     // DMA into the freed stage.
     auto step = [&](int kb, int stage) {
       __builtin_amdgcn_sched_barrier(0);
-      scales(f);
-      rows(stage);
+      chunk_scales();
+      float scp[C::FM];
+      rows(stage, scp);
       __builtin_amdgcn_sched_barrier(0);
-      last_row(stage ^ 1,
+      last_row(stage ^ 1, scp,
                [&] {
                  wait_vm_lgkm0<0>();
                  __builtin_amdgcn_s_barrier();
@@ -630,14 +696,37 @@ hipError_t launch_cfg(const GemmProblem& pr, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile choice.  The 256x256 tile needs about half the operand traffic per
-// MFMA of the 128x128 one, but it only pays off when there are enough tiles
-// to fill the 256 CUs.
+// Tile choice.  Workgroups go round-robin to the 8 XCDs of 32 CUs each; a
+// shape takes ceil(tiles per XCD / workgroup slots per XCD) rounds, each
+// costing about the time of one tile.  Relative tile costs (measured on
+// dense 8192x4096x7168): 256x256 = 1, 256x160 = 0.7, 128x128 at two
+// workgroups per CU = 0.52.  The 256x256 tile loads the fewest operand bytes
+// per MFMA and wins whenever it fills the chip.
+template <class C>
+double est_rounds(int64_t tiles, double cost) {
+  const int64_t per_xcd = (tiles + 7) / 8;
+  const int64_t slots = 32 * C::WG_PER_CU;
+  return (double)((per_xcd + slots - 1) / slots) * cost;
+}
+
 template <int MODE>
 hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
-  const int64_t rows = (MODE == kMasked) ? p.M * p.G : p.M;
-  const int64_t large_tiles = ((rows + 255) / 256) * ((p.N + 255) / 256);
-  if (large_tiles >= 256) return launch_cfg<LargeTile, MODE>(p, stream);
+  if (MODE == kMasked) {
+    // Memory-bound decode shapes: the large tile reads each weight panel once.
+    const int64_t large_tiles = ((p.M * p.G + 255) / 256) * ((p.N + 255) / 256);
+    if (large_tiles >= 256) return launch_cfg<LargeTile, MODE>(p, stream);
+    return launch_cfg<SmallTile, MODE>(p, stream);
+  }
+  // Row tiles: dense exact; contiguous counts on average half a partial tile
+  // per group.
+  auto mtiles = [&](int64_t bm) {
+    return MODE == kContiguous ? p.M / bm + (p.G + 1) / 2 : (p.M + bm - 1) / bm;
+  };
+  const double t_large = est_rounds<LargeTile>(mtiles(256) * ((p.N + 255) / 256), 1.0);
+  const double t_mid = est_rounds<MidTile>(mtiles(256) * ((p.N + 159) / 160), 0.7);
+  const double t_small = est_rounds<SmallTile>(mtiles(128) * ((p.N + 127) / 128), 0.52);
+  if (t_large <= t_mid && t_large <= t_small) return launch_cfg<LargeTile, MODE>(p, stream);
+  if (t_mid <= t_small) return launch_cfg<MidTile, MODE>(p, stream);
   return launch_cfg<SmallTile, MODE>(p, stream);
 }
 

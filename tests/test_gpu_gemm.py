@@ -51,19 +51,22 @@ def test_gemm_workload_recipe(M, N, K, out_dtype):
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_gemm_exact_integer_inputs_bit_exact(out_dtype):
+@pytest.mark.parametrize("M,N,K", [(256, 272, 1024),
+                                   # 256x160 tiles: a wave's columns straddle two weight blocks
+                                   (4000, 4112, 256)])
+def test_gemm_exact_integer_inputs_bit_exact(M, N, K, out_dtype):
     # codes with integer values in [-16, 16] and power-of-two scales: every
     # partial sum is exact in FP32, so the output is the one rounding of the
     # exact result.
+    print(f"exact-integer gemm M={M} N={N} K={K} out={out_dtype}", flush=True)
     rng = np.random.default_rng(0)
     vals = e4m3.decode(np.arange(256, dtype=np.uint8))
     ints = np.array([c for c in range(256) if np.isfinite(vals[c]) and vals[c] == np.round(vals[c])
                      and abs(vals[c]) <= 16 and c != 0x80], np.uint8)
-    M, N, K = 256, 272, 1024
     a = rng.choice(ints, (M, K)).astype(np.uint8)
     b = rng.choice(ints, (N, K)).astype(np.uint8)
     sa = (2.0 ** rng.integers(-2, 2, (K // 128, M))).astype(np.float32)
-    sb = (2.0 ** rng.integers(-2, 2, (3, K // 128))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-2, 2, ((N + 127) // 128, K // 128))).astype(np.float32)
     d = run(a, sa, b, sb, out_dtype)
     ref = gemm.gemm_ref(a, sa, b, sb, "bf16" if out_dtype == torch.bfloat16 else "f32")
     got = d.view(torch.int16).cpu().numpy().view(np.uint16) if out_dtype == torch.bfloat16 \
