@@ -51,16 +51,18 @@ __device__ __forceinline__ float pair_max(float v) { return dpp_max_step(v, 0); 
 // with a nonzero mantissa moves to the next exponent; a subnormal goes to the
 // next power-of-two bit pattern).
 //
-// fl32(x / s) is computed as  q0 = x*r;  e = fma(-q0, s, x);  y = fma(e, r, q0)
+// fl32(x / s) is computed as  q = x*r;  t = fma(q, s, -x);  y = fma(-t, r, q)
 // with r = RN(1/s) (a correctly rounded IEEE divide, once per tile).  This is
-// Markstein's correction step; it returns the correctly rounded quotient as
-// long as no operand or residual is subnormal.  Tiles with amax < 2^-60 are
-// therefore evaluated on x * 2^64 and s * 2^64 (both exact), which keeps every
-// operand normal; quotients that still come out subnormal encode to a zero
-// E4M3 code either way.  The resulting E4M3 codes were compared against
-// enc(x / s) for every pair of BF16 (x, amax) with |x| <= amax, for all
-// power-of-two scales, and for 6e8 random FP32 pairs: no difference.
-// ---------------------------------------------------------------------------
+// Markstein's correction step with the residual -t = x - q*s; it returns the
+// correctly rounded quotient as long as no operand or residual is subnormal.
+// Writing the residual with its sign flipped keeps the sign of a zero
+// quotient (x = -0 gives -0) without a separate copysign.  Tiles with
+// amax < 2^-60 are evaluated on x * 2^64 and s * 2^64 (both exact), which
+// keeps every operand normal; quotients that still come out subnormal encode
+// to a zero E4M3 code either way.  The resulting E4M3 codes, sign included,
+// were compared against enc(x / s) for every pair of BF16 (x, amax) with
+// |x| <= amax and both signs of x, for all power-of-two scales, and for 4e8
+// random FP32 pairs: no difference.
 struct TileScale {
   float s;    // the scale written to memory
   float ss;   // s * sx
@@ -91,29 +93,36 @@ __device__ __forceinline__ TileScale tile_scale(float amax) {
   return t;
 }
 
-// s > 0, so the quotient has the sign of x.  The correction step alone would
-// turn x = -0 into +0 (fma(+0, r, -0) = +0), hence the copysign.
+// s > 0.  For x = -0: q = -0, t = fma(-0, s, +0) = +0, y = fma(-0, r, -0) = -0.
 __device__ __forceinline__ float div_rn(float x, float s, float r) {
 #pragma clang fp contract(off)
-  float q = x * r;
-  float e = __builtin_fmaf(-q, s, x);
-  return __builtin_copysignf(__builtin_fmaf(e, r, q), x);
+  const float q = x * r;
+  const float t = __builtin_fmaf(q, s, -x);
+  return __builtin_fmaf(-t, r, q);
 }
 
 // ---------------------------------------------------------------------------
-// E4M3 encode of finite values that may exceed 448 by a rounding residue:
-// clamp to +-448 first (every value in (448, 464) rounds to 448 under RNE
-// anyway), then the hardware OCP-FP8 conversion (round to nearest even).
-// Packs four values into one dword, byte i = value i.
+// E4M3 encode (hardware OCP-FP8 conversion, round to nearest even), four
+// values into one dword, byte i = value i.
+//
+// pack4_e4m3 is for the quantizers, whose values satisfy |y| <= 448 * (1 +
+// 2^-22) < 464: the conversion rounds everything in [448, 464] to 448
+// (checked on the GPU for every FP32 value in that range), so no clamp is
+// needed.  pack4_e4m3_sat clamps to +-448 first (satfinite) for arbitrary
+// finite inputs.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float clamp448(float y) {
   return __builtin_fminf(__builtin_fmaxf(y, -kE4M3Max), kE4M3Max);
 }
 
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint32_t pack4_e4m3_sat(float a, float b, float c, float d) {
+  return pack4_e4m3(clamp448(a), clamp448(b), clamp448(c), clamp448(d));
 }
 
 // E4M3 byte `sel` of a dword -> float (exact).

@@ -37,11 +37,11 @@ __device__ __forceinline__ void nt_store8(void* p, uint2 v) {
 
 // ---------------------------------------------------------------------------
 // 1x128: one tile = 16 lanes (one DPP row) x 8 BF16 each (one 16-byte load).
-// A workgroup of 256 lanes covers 16 rows; each lane walks kTiles tiles of its
-// row so that kTiles loads are in flight before any arithmetic.  Scales of 16
+// A workgroup of 256 lanes covers 16 rows; each lane walks kQ1Tiles tiles of its
+// row so that kQ1Tiles loads are in flight before any arithmetic.  Scales of 16
 // consecutive rows are written together (s is [K/128][M], M contiguous).
 // ---------------------------------------------------------------------------
-constexpr int kQ1Tiles = 4;
+constexpr int kQ1Tiles = 2;
 
 template <bool POW2, bool SCALED>
 __device__ __forceinline__ uint2 quantize8(uint4 v, const TileScale& t) {
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void k_quantize_128x128(const uint16_t* __rest
 // Elementwise FP32 -> E4M3 with the quantizers' encoding; NaN keeps its sign.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t cast4(float4 v) {
-  uint32_t w = pack4_e4m3(v.x, v.y, v.z, v.w);
+  uint32_t w = pack4_e4m3_sat(v.x, v.y, v.z, v.w);
   const float e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
