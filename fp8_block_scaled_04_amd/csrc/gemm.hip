@@ -46,10 +46,12 @@ namespace {
 
 constexpr int kKC = 128;  // K chunk = promotion interval = MFMA K
 
-template <int BM_, int BN_, int WGM_, int WGN_, bool DB_>
+template <int BM_, int BN_, int WGM_, int WGN_, bool DB_, int S_ = 2, int PF_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
   static constexpr bool DB = DB_;                   // fragments double buffered in registers
+  static constexpr int S = S_;                      // LDS stages (chunks in flight + 1)
+  static constexpr int PF = PF_;                    // weight chunks prefetched into L2 beyond the stages
   static constexpr int NW = WGM * WGN;              // waves per workgroup
   static constexpr int THREADS = 64 * NW;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -70,19 +72,29 @@ struct Cfg {
   // in the last B instruction load nothing (zero-size descriptor) into a
   // scratch kilobyte of LDS after the two stages.
   static constexpr bool B_TAIL = BN % (8 * NW) != 0;
-  static constexpr int JUNK_OFF = 2 * STAGE;
-  static constexpr int LDS_BYTES = 2 * STAGE + (B_TAIL ? 1024 : 0);
+  static constexpr int JUNK_OFF = S * STAGE;
+  static constexpr int LDS_BYTES = S * STAGE + ((B_TAIL || PF > 0) ? 1024 : 0);
+  // L2 prefetch of a weight chunk: one dword per 64-byte half row, 32 rows
+  // per instruction, landing in the scratch kilobyte.
+  static constexpr int PF_LOADS = PF > 0 ? (BN + 32 * NW - 1) / (32 * NW) : 0;
   static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES;
   static_assert(BM % (8 * NW) == 0 && BN % 16 == 0, "A rows split evenly over the waves; B rows are fragments");
   static_assert(SA_WAVES < NW, "one wave must be left for the weight scales");
   static_assert(WN % 16 == 0 && WN <= 128, "a wave's columns are whole fragments within at most two weight blocks");
   static_assert(DB_ == false || 128 % WN == 0, "the double-buffered path needs a wave's columns in one weight block");
-  static_assert(LDS_BYTES <= 160 * 1024, "two stages must fit in LDS");
+  static_assert(LDS_BYTES <= 160 * 1024, "the stages must fit in LDS");
+  static_assert(S >= 2 && (!DB || S == 2), "the double-buffered path has two stages");
 };
 
 using SmallTile = Cfg<128, 128, 2, 2, true>;
 using LargeTile = Cfg<256, 256, 4, 2, false>;
 using MidTile = Cfg<256, 160, 4, 2, false>;
+// Memory-bound shapes (few rows): 128x96 tiles, three stages, one
+// workgroup per CU on the 24576-column decode projection.
+using StreamTile = Cfg<128, 96, 2, 2, false, 3>;
+// Masked (decode-time MoE) layout: weights of every non-empty expert stream
+// once.
+using MaskedTile = LargeTile;
 
 // LDS layout of an operand chunk: rows of 128 bytes (one K chunk), row-major,
 // with the 16-byte segments of row r XOR-swizzled: logical segment s is
@@ -344,7 +356,21 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     }
     dma4(rck, st + C::SA_OFF + wave * 256, sc_voff, soff);
   };
-  constexpr int DMA_PER_CHUNK = C::A_LOADS + C::B_LOADS + 1;   // vmcnt of one issue()
+  // Weight chunk kb into L2 (nothing is read back): lane l of instruction i
+  // touches row 32*(i*NW + wave) + l/2, half row l%2.  Rows past the tile
+  // fail the range check of the descriptor and fetch nothing.
+  auto prefetch = [&](int kb) {
+    if constexpr (C::PF > 0) {
+      const bool live = kb < KT;
+      const uint32_t koff = live ? (uint32_t)kb * kKC : 0u;
+      const v4i rbk = live ? rb : r_none;
+#pragma unroll
+      for (int i = 0; i < C::PF_LOADS; ++i)
+        dma4(rbk, smem_lds + C::JUNK_OFF, (uint32_t)((32 * (i * C::NW + wave) + (lane >> 1)) * K + (lane & 1) * 64),
+             koff);
+    }
+  };
+  constexpr int DMA_PER_CHUNK = C::A_LOADS + C::B_LOADS + 1 + C::PF_LOADS;   // vmcnt of one issue() + prefetch()
   // ---- per-lane fragment read offsets -----------------------------------
   const int fr = lane & 15, fg = lane >> 4;
   const uint32_t rd0 = fr * kKC + 16 * (fg ^ swz(fr));
@@ -615,12 +641,17 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) sa[j] = sa[j] * sb_lo;
     };
-    // Prologue: chunk 0 in stage 0, chunk 1 on its way to stage 1, chunk 0's
-    // first fragments read.
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
+    // Prologue: chunks 0 .. S-1 on their way to stages 0 .. S-1; once chunk
+    // 0 has landed in every wave's share, its first fragments are read.
+    constexpr int S = C::S;
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+      issue(c, c);
+      prefetch(S + c);
+    }
+    // chunks 1 .. S-1 (and their prefetches) may still be in flight
+    wait_vm_lgkm0<(S - 1) * DMA_PER_CHUNK + C::PF_LOADS>();
     __builtin_amdgcn_s_barrier();
-    issue(1, 1);
     read_a1(0, 0);
     read_b1(0, 0);
     read_sc(0);
@@ -628,29 +659,35 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     for (int j = 1; j < C::FM; ++j) read_a1(0, j);
     read_b1(0, 1);
     // Step kb (chunk kb in stage `stage`): rows 0 .. FN-2, then the last row,
-    // inside which the wave waits for chunk kb+1's DMA and meets the other
-    // waves (every wave then holds all of chunk kb in registers, so its stage
-    // is free), reads chunk kb+1's first fragments and starts chunk kb+2's
-    // DMA into the freed stage.
+    // inside which the wave waits for chunk kb+1's DMA (chunks kb+2 .. kb+S-1
+    // may still be in flight) and meets the other waves (every wave then
+    // holds all of chunk kb in registers, so its stage is free), reads chunk
+    // kb+1's first fragments and starts chunk kb+S's DMA into the freed
+    // stage.
     auto step = [&](int kb, int stage) {
       __builtin_amdgcn_sched_barrier(0);
       chunk_scales();
       float scp[C::FM];
       rows(stage, scp);
       __builtin_amdgcn_sched_barrier(0);
-      last_row(stage ^ 1, scp,
+      last_row(stage + 1 == S ? 0 : stage + 1, scp,
                [&] {
-                 wait_vm_lgkm0<0>();
+                 wait_vm_lgkm0<(S - 2) * DMA_PER_CHUNK + C::PF_LOADS>();
                  __builtin_amdgcn_s_barrier();
                },
-               [&] { issue(kb + 2, stage); });
+               [&] {
+                 issue(kb + S, stage);
+                 prefetch(kb + 2 * S);
+               });
     };
     int kb = 0;
-    for (; kb + 1 < KT; kb += 2) {
-      step(kb, 0);
-      step(kb + 1, 1);
+    for (; kb + S - 1 < KT; kb += S) {
+#pragma unroll
+      for (int st = 0; st < S; ++st) step(kb + st, st);
     }
-    if (kb < KT) step(kb, 0);
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+      if (kb + st < KT) step(kb + st, st);
   }
   __builtin_amdgcn_s_waitcnt(0);   // no LDS write may still be in flight at exit
 
@@ -714,8 +751,13 @@ hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
   if (MODE == kMasked) {
     // Memory-bound decode shapes: the large tile reads each weight panel once.
     const int64_t large_tiles = ((p.M * p.G + 255) / 256) * ((p.N + 255) / 256);
-    if (large_tiles >= 256) return launch_cfg<LargeTile, MODE>(p, stream);
+    if (large_tiles >= 256) return launch_cfg<MaskedTile, MODE>(p, stream);
     return launch_cfg<SmallTile, MODE>(p, stream);
+  }
+  // Few rows (decode): the weights stream from HBM once; a deep pipeline
+  // over many small tiles keeps enough bytes in flight.
+  if constexpr (MODE == kDense) {
+    if (p.M <= 128) return launch_cfg<StreamTile, MODE>(p, stream);
   }
   // Row tiles: dense exact; contiguous counts on average half a partial tile
   // per group.
