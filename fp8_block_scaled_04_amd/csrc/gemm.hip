@@ -67,18 +67,19 @@ struct Cfg {
   static constexpr int SB_OFF = A_BYTES + B_BYTES + SA_WAVES * 256;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   static constexpr int A_LOADS = BM / (8 * NW);     // 8 rows of 128 bytes per wave instruction
-  static constexpr int B_LOADS = (BN + 8 * NW - 1) / (8 * NW);
-  // When BN rows do not split evenly over the waves, the waves past the end
-  // in the last B instruction load nothing (zero-size descriptor) into a
-  // scratch kilobyte of LDS after the two stages.
-  static constexpr bool B_TAIL = BN % (8 * NW) != 0;
+  static constexpr int B_LOADS = BN / (8 * NW);     // whole 16-byte instructions
+  // Weight rows that do not split evenly over the waves (BN % (8 NW)) are
+  // loaded 4 bytes per lane: 2 rows per wave, 16 rows per instruction.
+  static constexpr int B_TAIL_ROWS = BN % (8 * NW);
+  static constexpr int B_TAIL_LOADS = B_TAIL_ROWS / (2 * NW);
   static constexpr int JUNK_OFF = S * STAGE;
-  static constexpr int LDS_BYTES = S * STAGE + ((B_TAIL || PF > 0) ? 1024 : 0);
+  static constexpr int LDS_BYTES = S * STAGE + (PF > 0 ? 1024 : 0);
   // L2 prefetch of a weight chunk: one dword per 64-byte half row, 32 rows
   // per instruction, landing in the scratch kilobyte.
   static constexpr int PF_LOADS = PF > 0 ? (BN + 32 * NW - 1) / (32 * NW) : 0;
   static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES;
   static_assert(BM % (8 * NW) == 0 && BN % 16 == 0, "A rows split evenly over the waves; B rows are fragments");
+  static_assert(B_TAIL_ROWS % (2 * NW) == 0, "the weight tail splits into 2-row pieces per wave");
   static_assert(SA_WAVES < NW, "one wave must be left for the weight scales");
   static_assert(WN % 16 == 0 && WN <= 128, "a wave's columns are whole fragments within at most two weight blocks");
   static_assert(DB_ == false || 128 % WN == 0, "the double-buffered path needs a wave's columns in one weight block");
@@ -188,6 +189,105 @@ struct GemmArgs {
   int32_t group_m;
 };
 
+// Operand bases and row ranges of the tile a workgroup computes.
+struct Tile {
+  const uint8_t* a_base;
+  const float* sa_base;
+  const uint8_t* b_base;
+  const float* sb_base;
+  int64_t m_alloc;     // rows that exist in memory (loads are clamped to them)
+  int64_t m_valid;     // rows that are computed and stored
+  int64_t sa_stride;   // distance between consecutive K chunks in sA
+  int64_t d_row0;      // first output row of this group's block of D
+  int64_t m0, n0;      // first row and column of the tile
+};
+
+// Workgroup -> tile.  Returns false for workgroups without work.
+template <int BM, int BN, int MODE>
+__device__ __forceinline__ bool map_tile(const GemmArgs& p, int64_t K, int KT, int64_t NB, Tile& t) {
+  // ---- tile -> (group, rows, columns) ------------------------------------
+  // The grouped layouts launch a grid sized for the worst case; the tiles
+  // that exist are counted here from the device-side group sizes, numbered
+  // 0 .. total-1, and spread evenly over the XCDs.
+  t.a_base = p.a;
+  t.sa_base = p.sa;
+  t.b_base = p.b;
+  t.sb_base = p.sb;
+  t.m_alloc = p.M;
+  t.m_valid = p.M;
+  t.sa_stride = p.M;
+  t.d_row0 = 0;
+  if (MODE == kMasked) {
+    // Tiles in group order; within a group, m fastest.
+    int total = 0;
+    for (int gg = 0; gg < p.G; ++gg) total += (int)((masked_count(p.groups[gg], p.M) + BM - 1) / BM);
+    total *= p.tiles_n;
+    int pid = xcd_remap((int)blockIdx.x, total);
+    if (pid < 0) return false;
+    int g = 0, cnt = 0;
+    int64_t rows = 0;
+    for (; g < p.G; ++g) {
+      rows = masked_count(p.groups[g], p.M);
+      cnt = (int)((rows + BM - 1) / BM) * p.tiles_n;
+      if (pid < cnt) break;
+      pid -= cnt;
+    }
+    const int tcnt = cnt / p.tiles_n;
+    const int tn = pid / tcnt, tm = pid - tn * tcnt;
+    t.m0 = (int64_t)tm * BM;
+    t.n0 = (int64_t)tn * BN;
+    t.m_valid = rows;
+    t.a_base += (int64_t)g * p.M * K;
+    t.sa_base += (int64_t)g * KT * p.M;
+    t.b_base += (int64_t)g * p.N * K;
+    t.sb_base += (int64_t)g * NB * KT;
+    t.d_row0 = (int64_t)g * p.M;
+  } else {
+    // Dense: the grid is exact.  Contiguous: tile t of group g has index
+    // (tiles of the groups before g) + t (group boundaries are multiples of
+    // 128 rows, so a tile never spans two groups).
+    int tiles_m = p.tiles_m;
+    if (MODE == kContiguous) {
+      tiles_m = 0;
+      for (int gg = 0; gg < p.G; ++gg) {
+        int64_t lo, hi;
+        group_rows(p.groups, gg, p.M, lo, hi);
+        tiles_m += (int)((hi - lo + BM - 1) / BM);
+      }
+    }
+    const int pid = xcd_remap((int)blockIdx.x, tiles_m * p.tiles_n);
+    if (pid < 0) return false;
+    // Walk the tiles in groups of group_m tile rows, column by column.
+    const int width = p.group_m * p.tiles_n;
+    const int grp = pid / width;
+    const int first_m = grp * p.group_m;
+    const int gsz = min(tiles_m - first_m, p.group_m);
+    const int r = pid - grp * width;
+    int tm = first_m + r % gsz;
+    const int tn = r / gsz;
+    t.n0 = (int64_t)tn * BN;
+    t.m0 = (int64_t)tm * BM;
+    if (MODE == kContiguous) {
+      int g = 0;
+      for (; g < p.G; ++g) {
+        int64_t lo, hi;
+        group_rows(p.groups, g, p.M, lo, hi);
+        const int cnt = (int)((hi - lo + BM - 1) / BM);
+        if (tm < cnt) {
+          t.m0 = lo + (int64_t)tm * BM;
+          t.m_valid = hi;
+          break;
+        }
+        tm -= cnt;
+      }
+      t.b_base += (int64_t)g * p.N * K;
+      t.sb_base += (int64_t)g * NB * KT;
+    }
+  }
+
+  return true;
+}
+
 template <int FM, int FN>
 struct Frags {
   v8i a[FM];
@@ -211,86 +311,14 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   const int KT = (int)(K / kKC);
   const int64_t NB = (N + 127) / 128;
 
-  // ---- tile -> (group, rows, columns) ------------------------------------
-  // The grouped layouts launch a grid sized for the worst case; the tiles
-  // that exist are counted here from the device-side group sizes, numbered
-  // 0 .. total-1, and spread evenly over the XCDs.
-  const uint8_t* a_base = p.a;
-  const float* sa_base = p.sa;
-  const uint8_t* b_base = p.b;
-  const float* sb_base = p.sb;
-  int64_t m_alloc = p.M;           // rows that exist in memory (loads are clamped to them)
-  int64_t m_valid = p.M;           // rows that are computed and stored
-  const int64_t sa_stride = p.M;   // distance between consecutive K chunks in sA
-  int64_t d_row0 = 0;              // first output row of this group's block of D
-  int64_t m0, n0;
-  if (MODE == kMasked) {
-    // Tiles in group order; within a group, m fastest.
-    int total = 0;
-    for (int gg = 0; gg < p.G; ++gg) total += (int)((masked_count(p.groups[gg], p.M) + BM - 1) / BM);
-    total *= p.tiles_n;
-    int pid = xcd_remap((int)blockIdx.x, total);
-    if (pid < 0) return;
-    int g = 0, cnt = 0;
-    int64_t rows = 0;
-    for (; g < p.G; ++g) {
-      rows = masked_count(p.groups[g], p.M);
-      cnt = (int)((rows + BM - 1) / BM) * p.tiles_n;
-      if (pid < cnt) break;
-      pid -= cnt;
-    }
-    const int tcnt = cnt / p.tiles_n;
-    const int tn = pid / tcnt, tm = pid - tn * tcnt;
-    m0 = (int64_t)tm * BM;
-    n0 = (int64_t)tn * BN;
-    m_valid = rows;
-    a_base += (int64_t)g * p.M * K;
-    sa_base += (int64_t)g * KT * p.M;
-    b_base += (int64_t)g * N * K;
-    sb_base += (int64_t)g * NB * KT;
-    d_row0 = (int64_t)g * p.M;
-  } else {
-    // Dense: the grid is exact.  Contiguous: tile t of group g has index
-    // (tiles of the groups before g) + t (group boundaries are multiples of
-    // 128 rows, so a tile never spans two groups).
-    int tiles_m = p.tiles_m;
-    if (MODE == kContiguous) {
-      tiles_m = 0;
-      for (int gg = 0; gg < p.G; ++gg) {
-        int64_t lo, hi;
-        group_rows(p.groups, gg, p.M, lo, hi);
-        tiles_m += (int)((hi - lo + BM - 1) / BM);
-      }
-    }
-    const int pid = xcd_remap((int)blockIdx.x, tiles_m * p.tiles_n);
-    if (pid < 0) return;
-    // Walk the tiles in groups of group_m tile rows, column by column.
-    const int width = p.group_m * p.tiles_n;
-    const int grp = pid / width;
-    const int first_m = grp * p.group_m;
-    const int gsz = min(tiles_m - first_m, p.group_m);
-    const int r = pid - grp * width;
-    int tm = first_m + r % gsz;
-    const int tn = r / gsz;
-    n0 = (int64_t)tn * BN;
-    m0 = (int64_t)tm * BM;
-    if (MODE == kContiguous) {
-      int g = 0;
-      for (; g < p.G; ++g) {
-        int64_t lo, hi;
-        group_rows(p.groups, g, p.M, lo, hi);
-        const int cnt = (int)((hi - lo + BM - 1) / BM);
-        if (tm < cnt) {
-          m0 = lo + (int64_t)tm * BM;
-          m_valid = hi;
-          break;
-        }
-        tm -= cnt;
-      }
-      b_base += (int64_t)g * N * K;
-      sb_base += (int64_t)g * NB * KT;
-    }
-  }
+  Tile t;
+  if (!map_tile<BM, BN, MODE>(p, K, KT, NB, t)) return;
+  const uint8_t* a_base = t.a_base;
+  const float* sa_base = t.sa_base;
+  const uint8_t* b_base = t.b_base;
+  const float* sb_base = t.sb_base;
+  const int64_t m_alloc = t.m_alloc, m_valid = t.m_valid, sa_stride = t.sa_stride, d_row0 = t.d_row0;
+  const int64_t m0 = t.m0, n0 = t.n0;
 
   // ---- buffer resources (SGPRs) and per-lane DMA offsets ------------------
   const int64_t a_rows = min<int64_t>(m_alloc - m0, BM);
@@ -344,15 +372,17 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     for (int i = 0; i < C::A_LOADS; ++i)
       dma16(rak, st + (i * C::NW + wave) * 8 * kKC, ro + i * row_step, koff);
 #pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i) {
-      const int r0 = (i * C::NW + wave) * 8;   // first of the 8 rows of this instruction
-      if (C::B_TAIL && i == C::B_LOADS - 1) {
-        const bool act = r0 < BN;
-        dma16(act ? rbk : r_none, act ? st + C::A_BYTES + r0 * kKC : smem_lds + C::JUNK_OFF, ro + i * row_step,
-              koff);
-      } else {
-        dma16(rbk, st + C::A_BYTES + r0 * kKC, ro + i * row_step, koff);
-      }
+    for (int i = 0; i < C::B_LOADS; ++i)
+      dma16(rbk, st + C::A_BYTES + (i * C::NW + wave) * 8 * kKC, ro + i * row_step, koff);
+    // Tail rows: instruction i, wave w covers rows t0 = B_LOADS*8*NW + 16i + 2w
+    // and t0+1; lane l writes LDS word l (row t0 + l/32, physical word l%32 of
+    // the swizzled row) from the logical segment that belongs there.
+#pragma unroll
+    for (int i = 0; i < C::B_TAIL_LOADS; ++i) {
+      const int t0 = C::B_LOADS * 8 * C::NW + 16 * i + 2 * wave;
+      const int row = t0 + (lane >> 5), pw = lane & 31;
+      const uint32_t voff = (uint32_t)(row * K + 16 * ((pw >> 2) ^ swz(row)) + 4 * (pw & 3));
+      dma4(rbk, st + C::A_BYTES + t0 * kKC, voff, koff);
     }
     dma4(rck, st + C::SA_OFF + wave * 256, sc_voff, soff);
   };
@@ -370,7 +400,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
              koff);
     }
   };
-  constexpr int DMA_PER_CHUNK = C::A_LOADS + C::B_LOADS + 1 + C::PF_LOADS;   // vmcnt of one issue() + prefetch()
+  constexpr int DMA_PER_CHUNK = C::A_LOADS + C::B_LOADS + C::B_TAIL_LOADS + 1 + C::PF_LOADS;   // vmcnt of one issue() + prefetch()
   // ---- per-lane fragment read offsets -----------------------------------
   const int fr = lane & 15, fg = lane >> 4;
   const uint32_t rd0 = fr * kKC + 16 * (fg ^ swz(fr));
@@ -589,11 +619,11 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     // The last row, split around the synchronisation: its first two MFMAs
     // (which need only this chunk's fragments) are issued before the wave
     // waits at the barrier, so the matrix core has work queued while the
-    // waves meet.  After the barrier, each MFMA frees its activation
-    // fragment, which is refilled with the next chunk's (from stage nstage);
-    // weight fragments 0 and 1 and the next chunk's scales follow, and
-    // `sync` (wait + barrier) and `mid` (the next DMA) run in between.  The
-    // FMAs keep this chunk's scales.
+    // waves meet; the other two right after it, before anything else.  Each
+    // MFMA frees its activation fragment, which is refilled with the next
+    // chunk's (from stage nstage); weight fragments 0 and 1 and the next
+    // chunk's scales follow, and `mid` (the next DMA) comes last.  The FMAs
+    // keep this chunk's scales.
     auto last_row = [&](int nstage, const float* scp, auto&& sync, auto&& mid) {
       float sc[C::FM];
       if (STRADDLE) row_scales(FN - 1, sc);
@@ -611,29 +641,28 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       sync();
       __builtin_amdgcn_sched_barrier(0);
+      // Two MFMAs in flight: blocks LAST+2 and LAST+3 use pc slots 0 and 1,
+      // which the FMAs of blocks LAST and LAST+1 have consumed (program
+      // order), so pc3 is a third result register.
+      const v4f p2 = mfma(LAST + 2);
+      __builtin_amdgcn_sched_barrier(0);
       read_a1(nstage, 0);
       read_b1(nstage, 0);
       __builtin_amdgcn_sched_barrier(0);
       read_sc(nstage);
       __builtin_amdgcn_sched_barrier(0);
+      const v4f p3 = mfma(LAST + 3);
+      __builtin_amdgcn_sched_barrier(0);
       read_a1(nstage, 1);
       read_b1(nstage, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mid();
-      __builtin_amdgcn_sched_barrier(0);
-      pc[(LAST + 2) & 1] = mfma(LAST + 2);
       read_a1(nstage, 2);
       fma_block(LAST + 1, pc[(LAST + 1) & 1], sc);
-      pc[(LAST + 3) & 1] = mfma(LAST + 3);
+      fma_block(LAST + 2, p2, sc);
+      __builtin_amdgcn_sched_barrier(0);
       read_a1(nstage, 3);
-      fma_block(LAST + 2, pc[(LAST + 2) & 1], sc);
-      fma_block(LAST + 3, pc[(LAST + 3) & 1], sc);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      fma_block(LAST + 3, p3, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      mid();
     };
     // Without straddling, every row uses sa * sb: multiply once per chunk.
     auto chunk_scales = [&] {
