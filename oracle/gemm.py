@@ -22,6 +22,17 @@ Grouped layouts:
               [m_offsets[g], m_offsets[g+1]) and uses B[g], sB[g].
   masked:     A[G][cap][K]; group g uses only its first masked_m[g] rows.
 Rows that belong to no group are reported as NaN (not compared).
+
+Weight gradient (page 1, paragraphs on caching FP8 activations and converting
+1x128 tiles to 128x1 tiles for the backward pass): dW = dY^T X contracts over
+tokens, so both operands are quantized along the token dimension -- dY^T and
+X^T with one scale per 128 tokens of each row (the 128x1 tiles of dY and X,
+i.e. the output of the transpose-requantize step).  As an "NT" GEMM:
+
+    D[m][n] = sum_kb  sA[kb][m] * sB[kb][n] * sum_{k in kb} dec(A[m][k]) * dec(B[n][k])
+
+with A[M][K], sA[K/128][M], B[N][K], sB[K/128][N] (K = tokens), FP32 out,
+optionally added to an existing FP32 D (gradient accumulation).
 """
 
 import numpy as np
@@ -108,6 +119,21 @@ def gemm_block_f64(a, sa, b, sb, rows, cols) -> np.ndarray:
     Bs = np.asarray(sb)[cols // TILE]
     B = e4m3.decode(Bq) * np.repeat(Bs.astype(np.float64), TILE, axis=1)
     return A @ B.T
+
+
+def wgrad_f64(a, sa, b, sb) -> np.ndarray:
+    """Weight-gradient GEMM in float64: both operands dequantized with one
+    scale per row per 128 K (the activation-style layout [K/128][rows])."""
+    return dequant_a(a, sa) @ dequant_a(b, sb).T
+
+
+def wgrad_ref(a, sa, b, sb, d_in=None) -> np.ndarray:
+    """FP32 weight gradient: fl32(sum), or with accumulation fl32(d_in + sum)
+    (the float64 total rounded once)."""
+    d = wgrad_f64(a, sa, b, sb)
+    if d_in is not None:
+        d = d + np.asarray(d_in, np.float32).astype(np.float64)
+    return d.astype(np.float32)
 
 
 def grouped_contiguous_f64(a, sa, b, sb, m_offsets) -> np.ndarray:

@@ -144,3 +144,66 @@ def test_grouped_masked_counts():
     np.testing.assert_array_equal(d[1], gemm.gemm_f64(a[1], sa[1], b[1], sb[1]))
     np.testing.assert_array_equal(d[2, :77], gemm.gemm_f64(a[2, :77], sa[2][:, :77], b[2], sb[2]))
     assert np.isnan(d[2, 77:]).all()
+
+
+# ---- weight-gradient reference ---------------------------------------------
+
+def test_wgrad_fraction_brute_force_small():
+    # both operands scaled per row and per 128 K; exact rational sums
+    rng = np.random.default_rng(11)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    M, N, K = 3, 2, 384
+    a = rng.choice(finite, (M, K))
+    b = rng.choice(finite, (N, K))
+    sa = rng.uniform(1e-3, 2.0, (K // 128, M)).astype(np.float32)
+    sb = rng.uniform(1e-3, 2.0, (K // 128, N)).astype(np.float32)
+    d_in = rng.standard_normal((M, N)).astype(np.float32)
+    got = gemm.wgrad_ref(a, sa, b, sb)
+    got_acc = gemm.wgrad_ref(a, sa, b, sb, d_in)
+    av, bv = tdec(a), tdec(b)
+    for m in range(M):
+        for n in range(N):
+            tot = sum(Fraction(float(av[m, k])) * Fraction(float(sa[k // 128, m]))
+                      * Fraction(float(bv[n, k])) * Fraction(float(sb[k // 128, n])) for k in range(K))
+            assert abs(Fraction(float(got[m, n])) - tot) <= abs(tot) * Fraction(1, 2 ** 24)
+            tot_acc = tot + Fraction(float(d_in[m, n]))
+            assert abs(Fraction(float(got_acc[m, n])) - tot_acc) <= abs(tot_acc) * Fraction(1, 2 ** 24)
+
+
+def test_wgrad_exact_integer_sums():
+    # integer-valued codes, power-of-two scales: Python-integer sums are exact
+    rng = np.random.default_rng(12)
+    ints = integer_codes()
+    M, N, K = 5, 7, 256
+    a = rng.choice(ints, (M, K))
+    b = rng.choice(ints, (N, K))
+    sa = (2.0 ** rng.integers(-3, 3, (K // 128, M))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-3, 3, (K // 128, N))).astype(np.float32)
+    av, bv = tdec(a).astype(np.int64), tdec(b).astype(np.int64)
+    got = gemm.wgrad_ref(a, sa, b, sb)
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for kb in range(K // 128):
+                chunk = int(sum(int(av[m, k]) * int(bv[n, k]) for k in range(kb * 128, kb * 128 + 128)))
+                tot += chunk * Fraction(float(sa[kb, m])) * Fraction(float(sb[kb, n]))
+            assert Fraction(float(got[m, n])) == tot          # |sum| < 2^24: exact in FP32
+
+
+def test_wgrad_transposed_scale_layout_is_distinct():
+    # a transposed sB (the [rows][K/128] layout) changes the result: the
+    # reference reads sB as [K/128][N]
+    rng = np.random.default_rng(13)
+    ints = integer_codes()
+    a = rng.choice(ints, (4, 256))
+    b = rng.choice(ints, (2, 256))
+    sa = np.ones((2, 4), np.float32)
+    sb = np.array([[1.0, 2.0], [4.0, 8.0]], np.float32)     # [K/128][N]
+    ref = gemm.wgrad_f64(a, sa, b, sb)
+    av, bv = tdec(a), tdec(b)
+    expect = np.zeros((4, 2))
+    for kb in range(2):
+        sl = slice(kb * 128, kb * 128 + 128)
+        expect += (av[:, sl] @ bv[:, sl].T) * sb[kb][None, :]
+    assert np.array_equal(ref, expect)
+    assert not np.array_equal(gemm.wgrad_f64(a, sa, b, sb.T.copy()), expect)
