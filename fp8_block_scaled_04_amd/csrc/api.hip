@@ -129,7 +129,21 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const
   if (M == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, nullptr, false)) return e;
   if (fp8bs_status e = check_device()) return e;
-  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, out_dtype == FP8BS_OUT_FP32, fp8bs::kDense};
+  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, out_dtype == FP8BS_OUT_FP32, false, fp8bs::kDense};
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_gemm_fp8_wgrad(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, float* d,
+                                  int64_t M, int64_t N, int64_t K, int32_t accumulate, fp8bs_stream_t stream) {
+  if (M < 0) return FP8BS_ERR_SHAPE;
+  if (fp8bs_status e = gemm_common(N, K, FP8BS_OUT_FP32)) return e;
+  if (!grid_fits(M, N, 1)) return FP8BS_ERR_SHAPE;
+  if (accumulate != 0 && accumulate != 1) return FP8BS_ERR_FLAGS;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, nullptr, false)) return e;
+  if (fp8bs_status e = check_device()) return e;
+  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, true, accumulate == 1, fp8bs::kWgrad};
   (void)hipGetLastError();
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
 }
@@ -143,7 +157,7 @@ fp8bs_status fp8bs_grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa
   if (G == 0 || Mt == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, m_offsets, true)) return e;
   if (fp8bs_status e = check_device()) return e;
-  GemmProblem p{a, sa, b, sb, d, m_offsets, Mt, N, K, G, out_dtype == FP8BS_OUT_FP32, fp8bs::kContiguous};
+  GemmProblem p{a, sa, b, sb, d, m_offsets, Mt, N, K, G, out_dtype == FP8BS_OUT_FP32, false, fp8bs::kContiguous};
   (void)hipGetLastError();
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
 }
@@ -157,7 +171,7 @@ fp8bs_status fp8bs_grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, co
   if (G == 0 || cap == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, masked_m, true)) return e;
   if (fp8bs_status e = check_device()) return e;
-  GemmProblem p{a, sa, b, sb, d, masked_m, cap, N, K, G, out_dtype == FP8BS_OUT_FP32, fp8bs::kMasked};
+  GemmProblem p{a, sa, b, sb, d, masked_m, cap, N, K, G, out_dtype == FP8BS_OUT_FP32, false, fp8bs::kMasked};
   (void)hipGetLastError();
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
 }

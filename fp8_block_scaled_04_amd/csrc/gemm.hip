@@ -187,6 +187,7 @@ struct GemmArgs {
   int32_t G;
   int32_t tiles_m, tiles_n;   // dense: tile grid; grouped: per-group / worst-case bound
   int32_t group_m;
+  int32_t accumulate;         // kWgrad: add to D
 };
 
 // Operand bases and row ranges of the tile a workgroup computes.
@@ -217,7 +218,7 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int64_t K, int KT, i
   t.m_valid = p.M;
   t.sa_stride = p.M;
   t.d_row0 = 0;
-  if (MODE == kMasked) {
+  if constexpr (MODE == kMasked) {
     // Tiles in group order; within a group, m fastest.
     int total = 0;
     for (int gg = 0; gg < p.G; ++gg) total += (int)((masked_count(p.groups[gg], p.M) + BM - 1) / BM);
@@ -342,14 +343,22 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   // Scale DMA of this wave (one dword per lane per chunk, no branches):
   // waves below SA_WAVES fetch activation scales of rows m0 + 64*wave + lane,
   // the others the weight scale of block row n0/128 + lane (both clamped).
+  // (kWgrad: the other waves fetch weight-row scales n0 + 64*(wave -
+  // SA_WAVES) + lane from the [K/128][N] layout, landing right after the
+  // activation scales.)
   const bool sa_wave = wave < C::SA_WAVES;
   int64_t sa_row = m0 + (sa_wave ? wave : 0) * 64 + lane;
   if (sa_row > m_alloc - 1) sa_row = m_alloc - 1;
   int64_t sb_blk = n0 / 128 + lane;
   if (sb_blk > NB - 1) sb_blk = NB - 1;
-  const v4i rsc = sa_wave ? rsa : rsb;
-  const uint32_t sc_voff = sa_wave ? (uint32_t)(sa_row * 4) : (uint32_t)(sb_blk * KT * 4);
-  const uint32_t sc_step = __builtin_amdgcn_readfirstlane(sa_wave ? (uint32_t)(sa_stride * 4) : 4u);
+  int64_t sb_row = n0 + (sa_wave ? 0 : wave - C::SA_WAVES) * 64 + lane;
+  if (sb_row > N - 1) sb_row = N - 1;
+  const v4i rsb_w = make_rsrc(sb_base, (int64_t)KT * N * 4);
+  const v4i rsc = sa_wave ? rsa : (MODE == kWgrad ? rsb_w : rsb);
+  const uint32_t sc_voff = sa_wave ? (uint32_t)(sa_row * 4)
+                                   : (MODE == kWgrad ? (uint32_t)(sb_row * 4) : (uint32_t)(sb_blk * KT * 4));
+  const uint32_t sc_step = __builtin_amdgcn_readfirstlane(
+      sa_wave ? (uint32_t)(sa_stride * 4) : (MODE == kWgrad ? (uint32_t)(N * 4) : 4u));
 
   // Chunks past the end (the pipeline issues ahead) use descriptors with
   // zero records: every lane is out of range, so the hardware writes zeros
@@ -487,6 +496,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   // reads fragments and computes.  Past the last chunk the DMA goes through
   // the zero-record descriptor and reads touch a stale stage.
   if constexpr (C::DB) {
+    static_assert(MODE != kWgrad, "the weight gradient runs on the 256-wide tiles");
     // Two fragment sets: chunk kb's fragments were read in the previous
     // step; read chunk kb+1's while computing chunk kb.
     F f0, f1;
@@ -533,7 +543,17 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     constexpr bool STRADDLE = (128 % C::WN) != 0;
     static_assert(C::WN <= 128, "a wave's columns span at most two weight blocks");
     v8i fa[C::FM], fb[SLOTS];
-    float sa[C::FM];          // activation scales (times the weight scale unless STRADDLE)
+    float sa[C::FM];          // activation scales (times the weight scale unless STRADDLE or ROWB)
+    // Weight gradient (ROWB): every weight row has its own scale; the scales
+    // of weight fragment i's four columns (of this lane) are a float4, read
+    // during row i-1 (after its first block's FMAs, which free the slot of
+    // row i-2) into slot i % 2.  The next chunk's row 0 goes to slot 0
+    // during the last row, so with an odd FN the last row takes slot 2.
+    constexpr bool ROWB = MODE == kWgrad;
+    static_assert(!ROWB || C::FM >= 2, "the weight scales are read at a row's second block");
+    static_assert(!ROWB || BN <= (C::NW - C::SA_WAVES) * 64, "the scale waves must cover every weight row");
+    float4 sbr[3];
+    auto sslot = [](int i) { return (i == FN - 1 && (FN - 1) % 2 == 0) ? 2 : i % 2; };
     float sb_lo = 0.f, sb_hi = 0.f;
     const int blk_lo = sb_idx;
     const int blk_hi = (int)((n0 + b_row0 + C::WN - 1) / 128 - n0 / 128);
@@ -553,11 +573,19 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       const uint8_t* st = smem + stage * C::STAGE;
 #pragma unroll
       for (int j = 0; j < C::FM; ++j) sa[j] = reinterpret_cast<const float*>(st + C::SA_OFF)[a_row0 + 16 * j + fr];
-      sb_lo = reinterpret_cast<const float*>(st + C::SB_OFF)[blk_lo];
-      if (STRADDLE) sb_hi = reinterpret_cast<const float*>(st + C::SB_OFF)[blk_hi];
+      if (!ROWB) sb_lo = reinterpret_cast<const float*>(st + C::SB_OFF)[blk_lo];
+      if (STRADDLE && !ROWB) sb_hi = reinterpret_cast<const float*>(st + C::SB_OFF)[blk_hi];
+    };
+    auto read_sbr = [&](int stage, int i) {
+      sbr[sslot(i)] = *reinterpret_cast<const float4*>(smem + stage * C::STAGE + C::SB_OFF + 4 * (b_row0 + 16 * i + 4 * fg));
     };
     // Scale products of weight fragment i: sa * sb(block of fragment i).
     auto row_scales = [&](int i, float* sc) {
+      if (ROWB) {
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) sc[j] = sa[j];
+        return;
+      }
       const bool hi_blk = (int)((n0 + b_row0 + 16 * i) / 128 - n0 / 128) != blk_lo;
       const float sbi = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
                             __builtin_bit_cast(int, hi_blk ? sb_hi : sb_lo)));
@@ -575,15 +603,22 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     };
     auto fma_block = [&](int b, const v4f& pv, const float* sc) {
       v4f& ac = acc[b / C::FM][b % C::FM];
+      if (ROWB) {
+        const float4 sv = sbr[sslot(b / C::FM)];
+        const float sw[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ac[r] = __builtin_fmaf(pv[r], sc[b % C::FM], ac[r]);
+        for (int r = 0; r < 4; ++r) ac[r] = __builtin_fmaf(pv[r], sc[b % C::FM] * sw[r], ac[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ac[r] = __builtin_fmaf(pv[r], sc[b % C::FM], ac[r]);
+      }
     };
     // Rows 0 .. FN-2; weight fragment i+2 is read at the start of row i.
     // Returns, in scl, the scale products of row FN-2 (its last block's FMAs
     // run in the last row).
     auto rows = [&](int stage, float* scl) {
       float sc[2][C::FM];
-      if (STRADDLE) row_scales(0, sc[0]);
+      if (STRADDLE || ROWB) row_scales(0, sc[0]);
       else
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) sc[0][j] = sa[j];
@@ -593,9 +628,10 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       for (int b = 1; b < LAST; ++b) {
         const int i = b / C::FM;
         pc[b & 1] = mfma(b);
+        if (ROWB && b % C::FM == 1 && i + 1 < FN) read_sbr(stage, i + 1);
         if (b % C::FM == 0) {
           if (i + 2 < FN) read_b1(stage, i + 2);
-          if (STRADDLE) row_scales(i, sc[i & 1]);
+          if (STRADDLE || ROWB) row_scales(i, sc[i & 1]);
           else
 #pragma unroll
             for (int j = 0; j < C::FM; ++j) sc[i & 1][j] = sa[j];
@@ -611,8 +647,10 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
 #pragma unroll
       for (int b = 1; b < LAST; ++b) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ROWB && b % C::FM == 1 && b / C::FM + 1 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         if (b % C::FM == 0 && b / C::FM + 2 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        if (STRADDLE && b % C::FM == 0) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        if (ROWB) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        else if (STRADDLE && b % C::FM == 0) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         else __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
     };
@@ -626,7 +664,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     // keep this chunk's scales.
     auto last_row = [&](int nstage, const float* scp, auto&& sync, auto&& mid) {
       float sc[C::FM];
-      if (STRADDLE) row_scales(FN - 1, sc);
+      if (STRADDLE || ROWB) row_scales(FN - 1, sc);
       else
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) sc[j] = sa[j];
@@ -635,9 +673,9 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       pc[(LAST + 1) & 1] = mfma(LAST + 1);
       fma_block(LAST, pc[LAST & 1], sc);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, STRADDLE ? 8 : 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, (STRADDLE || ROWB) ? 8 : 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, ROWB ? 8 : 4, 0);
       __builtin_amdgcn_sched_barrier(0);
       sync();
       __builtin_amdgcn_sched_barrier(0);
@@ -650,6 +688,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       read_b1(nstage, 0);
       __builtin_amdgcn_sched_barrier(0);
       read_sc(nstage);
+      if (ROWB) read_sbr(nstage, 0);
       __builtin_amdgcn_sched_barrier(0);
       const v4f p3 = mfma(LAST + 3);
       __builtin_amdgcn_sched_barrier(0);
@@ -666,7 +705,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     };
     // Without straddling, every row uses sa * sb: multiply once per chunk.
     auto chunk_scales = [&] {
-      if (!STRADDLE)
+      if (!STRADDLE && !ROWB)
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) sa[j] = sa[j] * sb_lo;
     };
@@ -684,6 +723,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     read_a1(0, 0);
     read_b1(0, 0);
     read_sc(0);
+    if (ROWB) read_sbr(0, 0);
 #pragma unroll
     for (int j = 1; j < C::FM; ++j) read_a1(0, j);
     read_b1(0, 1);
@@ -730,8 +770,13 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       if (m < m_valid && n < N) {
         const int64_t idx = (d_row0 + m) * N + n;
         if (OUT_F32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.d) + idx) =
-              make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+          float4* dp = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.d) + idx);
+          float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+          if (MODE == kWgrad && p.accumulate) {
+            const float4 o = *dp;
+            v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+          }
+          *dp = v;
         } else {
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.d) + idx) =
               make_uint2(pack2_bf16(acc[i][j][0], acc[i][j][1]), pack2_bf16(acc[i][j][2], acc[i][j][3]));
@@ -753,11 +798,12 @@ hipError_t launch_cfg(const GemmProblem& pr, hipStream_t stream) {
   if (MODE == kContiguous) a.tiles_m = (int32_t)(pr.M / C::BM + pr.G);
   a.tiles_n = (int32_t)((pr.N + C::BN - 1) / C::BN);
   a.group_m = 8;
+  a.accumulate = pr.accumulate ? 1 : 0;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * (MODE == kMasked ? pr.G : 1);
   if (blocks == 0) return hipSuccess;
-  if (pr.out_f32)
+  if (MODE == kWgrad || pr.out_f32)
     hipLaunchKernelGGL((k_gemm<C, MODE, true>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
-  else
+  else if constexpr (MODE != kWgrad)   // the weight gradient is FP32 only
     hipLaunchKernelGGL((k_gemm<C, MODE, false>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
   return hipGetLastError();
 }
@@ -777,7 +823,7 @@ double est_rounds(int64_t tiles, double cost) {
 
 template <int MODE>
 hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
-  if (MODE == kMasked) {
+  if constexpr (MODE == kMasked) {
     // Memory-bound decode shapes: the large tile reads each weight panel once.
     const int64_t large_tiles = ((p.M * p.G + 255) / 256) * ((p.N + 255) / 256);
     if (large_tiles >= 256) return launch_cfg<MaskedTile, MODE>(p, stream);
@@ -796,9 +842,15 @@ hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
   const double t_large = est_rounds<LargeTile>(mtiles(256) * ((p.N + 255) / 256), 1.0);
   const double t_mid = est_rounds<MidTile>(mtiles(256) * ((p.N + 159) / 160), 0.7);
   const double t_small = est_rounds<SmallTile>(mtiles(128) * ((p.N + 127) / 128), 0.52);
-  if (t_large <= t_mid && t_large <= t_small) return launch_cfg<LargeTile, MODE>(p, stream);
-  if (t_mid <= t_small) return launch_cfg<MidTile, MODE>(p, stream);
-  return launch_cfg<SmallTile, MODE>(p, stream);
+  if constexpr (MODE == kWgrad) {
+    // per-row weight scales are read in the 256-wide tiles' loop only
+    if (t_large <= t_mid) return launch_cfg<LargeTile, MODE>(p, stream);
+    return launch_cfg<MidTile, MODE>(p, stream);
+  } else {
+    if (t_large <= t_mid && t_large <= t_small) return launch_cfg<LargeTile, MODE>(p, stream);
+    if (t_mid <= t_small) return launch_cfg<MidTile, MODE>(p, stream);
+    return launch_cfg<SmallTile, MODE>(p, stream);
+  }
 }
 
 }  // namespace
@@ -807,6 +859,7 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
   switch (p.mode) {
     case kDense: return dispatch<kDense>(p, stream);
     case kContiguous: return dispatch<kContiguous>(p, stream);
+    case kWgrad: return dispatch<kWgrad>(p, stream);
     default: return dispatch<kMasked>(p, stream);
   }
 }

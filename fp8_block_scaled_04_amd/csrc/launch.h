@@ -15,19 +15,22 @@ hipError_t launch_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t 
                                    hipStream_t stream);
 hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream);
 
-enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2 };
+// kWgrad: dense layout, but B carries one scale per row per 128 K ([K/128][N],
+// like A) and D is FP32, optionally accumulated into.
+enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2, kWgrad = 3 };
 
 struct GemmProblem {
   const uint8_t* a;       // E4M3 activations
   const float* sa;        // 1x128 scales
   const uint8_t* b;       // E4M3 weights ([G][N][K] for grouped)
-  const float* sb;        // 128x128 scales
+  const float* sb;        // 128x128 scales (kWgrad: 1x128 scales [K/128][N])
   void* d;                // output
   const int32_t* groups;  // m_offsets [G+1] (contiguous) or masked_m [G] (masked); device
   int64_t M;              // rows: dense M, contiguous Mt, masked cap
   int64_t N, K;
   int32_t G;              // number of groups (1 for dense)
   bool out_f32;
+  bool accumulate;        // kWgrad: D += A B^T
   GemmMode mode;
 };
 

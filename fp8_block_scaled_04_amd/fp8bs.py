@@ -42,6 +42,7 @@ _q1x128 = _sig("fp8bs_quantize_1x128", [_P, _I64, _I64, _P, _P, _U32, _P])
 _qt = _sig("fp8bs_quantize_transpose_128x1", [_P, _P, _I64, _I64, _P, _P, _U32, _P])
 _q128 = _sig("fp8bs_quantize_128x128", [_P, _I64, _I64, _I64, _P, _P, _U32, _P])
 _gemm = _sig("fp8bs_gemm_fp8_blockscaled", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P])
+_wgrad = _sig("fp8bs_gemm_fp8_wgrad", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P])
 _gcont = _sig("fp8bs_grouped_gemm_fp8_contiguous",
               [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P])
 _gmask = _sig("fp8bs_grouped_gemm_fp8_masked",
@@ -174,6 +175,35 @@ def gemm(a, sa, b, sb, out_dtype=torch.bfloat16, out=None):
             raise ValueError("out has the wrong shape")
     _check(_gemm(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, code, _stream(a)),
            "gemm_fp8_blockscaled")
+    return out
+
+
+def gemm_wgrad(a, sa, b, sb, out=None, accumulate=False):
+    """Weight gradient D[M][N] (FP32) = A * B^T, K = tokens, both operands with
+    one scale per row per 128 K: sa[K/128][M], sb[K/128][N] (the layout the
+    transpose-requantize step produces).  With accumulate=True the product is
+    added to `out`."""
+    _codes(a, "a"); _codes(b, "b")
+    for t, n in ((a, "a"), (b, "b")):
+        _need(t, n, None, 2)
+    _need(sa, "sa", torch.float32, 2)
+    _need(sb, "sb", torch.float32, 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must share K")
+    if tuple(sa.shape) != (K // 128, M) or tuple(sb.shape) != (K // 128, N):
+        raise ValueError("scale shapes do not match the operands")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out")
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    else:
+        _need(out, "out", torch.float32, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    _check(_wgrad(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, 1 if accumulate else 0, _stream(a)),
+           "gemm_fp8_wgrad")
     return out
 
 

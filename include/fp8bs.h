@@ -143,6 +143,24 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa,
                                         int32_t out_dtype, fp8bs_stream_t stream);
 
 /*
+ * Weight-gradient GEMM (page 1, paragraphs on caching FP8 activations and on
+ * converting 1x128 tiles to 128x1 tiles for the backward pass): dW = dY^T X
+ * contracts over tokens, so both operands carry one scale per row per 128
+ * tokens -- the transposed, requantized activations that
+ * fp8bs_quantize_transpose_128x1 produces.  D = A * B^T in FP32, K = tokens.
+ *   a  : E4M3 [M][K],   sa : FP32 [K/128][M]     (e.g. dY^T: M = output features)
+ *   b  : E4M3 [N][K],   sb : FP32 [K/128][N]     (e.g. X^T:  N = input features)
+ *   d  : FP32 [M][N]; accumulate = 1 adds the product to d's contents
+ *        (gradient accumulation), 0 overwrites them.
+ * Requires M >= 0, N >= 0, N % 16 == 0, K > 0, K % 128 == 0, accumulate in
+ * {0, 1} (else FP8BS_ERR_FLAGS).
+ */
+fp8bs_status fp8bs_gemm_fp8_wgrad(const uint8_t* a, const float* sa,
+                                  const uint8_t* b, const float* sb,
+                                  float* d, int64_t M, int64_t N, int64_t K,
+                                  int32_t accumulate, fp8bs_stream_t stream);
+
+/*
  * Grouped GEMM, contiguous MoE layout (page 4, section "Schluesselmerkmale
  * von DeepGemm", the first of the two MoE layouts): the rows of every group
  * are concatenated; group g owns rows [m_offsets[g], m_offsets[g+1]) of A and

@@ -34,7 +34,7 @@ def lib(lib_path):
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in fp8bs.h but not exported"
 
@@ -139,3 +139,15 @@ def test_binding_imports_and_reports_its_library(lib_path):
     from fp8_block_scaled_04_amd import fp8bs
     assert fp8bs.library() == lib_path
     assert fp8bs.abi_version() == 1
+
+
+def test_wgrad_validation(lib):
+    f = fn(lib, "fp8bs_gemm_fp8_wgrad", [P, P, P, P, P, I64, I64, I64, I32, P])
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 24, 128, 0, None) == SHAPE     # N % 16
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 100, 0, None) == SHAPE     # K % 128
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 32, 128, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 2, None) == FLAGS     # accumulate in {0, 1}
+    assert f(None, None, None, None, None, 0, 32, 128, 0, None) == OK        # empty
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 4, 32, 128, 1, None) == NULL
+    assert f(FAKE, FAKE, FAKE, MIS, FAKE, 4, 32, 128, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 1, None) == DEVICE
