@@ -15,6 +15,13 @@ What they compute, and where it comes from:
   input channels.  The pages only ask for scaling per group inside the MMA
   (page 2, "A Deadly Mistake Uncovered on Deepseek China Ai", paragraph on
   hardware suggestions); the block shape is the workload's.
+* Transposed weights: page 2, paragraph on hardware suggestions, asks for
+  GEMMs on transposed operands.  The data gradient dX = dY W needs the
+  weight transposed; a 128x128-block-scaled weight transposed is again
+  block-scaled with the same codes and the transposed scale grid, so no
+  requantization is involved.  Rows of W past the last multiple of 128 (a
+  ragged N) become zero columns, so the transposed weight's K is a multiple
+  of 128 (the activation gradient is quantized over the same padded width).
 * Power-of-two scales: page 2, same paragraph as the 14-bit accumulation
   note, says some activations use scaling factors that are integral powers of
   two.  Read here as: round the FP32 scale UP to the next power of two, so no
@@ -34,6 +41,8 @@ Scale layouts (row-major, M contiguous for activations):
   quantize_1x128            x[R][C]  -> q[R][C],  s[C/128][R]
   quantize_transpose_128x1  q[M][K], s[K/128][M] -> qt[K][M], st[M/128][K]
   quantize_128x128          w[N][K]  -> q[N][K],  s[ceil(N/128)][K/128]
+  transpose_128x128         q[N][K], s[ceil(N/128)][K/128] -> qt[K][Np], st[K/128][Np/128],
+                            Np = 128 * ceil(N/128)
 """
 
 import numpy as np
@@ -134,3 +143,24 @@ def quantize_128x128(w_bf16_bits, pow2: bool = False):
         s[i] = tile_scale(amax, pow2)
         q[i * TILE:(i + 1) * TILE] = quantize_values(blocks, s[i][None, :, None]).reshape(rows.shape[0], K)
     return q, s
+
+
+def transpose_128x128(q, s):
+    """Block-scaled weight q[N][K], s[ceil(N/128)][K/128] (or [G][...]) ->
+    the transposed weight as a block-scaled weight of the same kind:
+    qt[K][Np] with qt[k][n] = q[n][k] for n < N and zero codes for
+    N <= n < Np = 128*ceil(N/128); st[kb][nb] = s[nb][kb]."""
+    q = np.asarray(q, dtype=np.uint8)
+    s = np.asarray(s, dtype=np.float32)
+    if q.ndim == 3:
+        outs = [transpose_128x128(q[g], s[g]) for g in range(q.shape[0])]
+        return np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs])
+    N, K = q.shape
+    if K % TILE:
+        raise ValueError("K must be a multiple of 128")
+    nb = -(-N // TILE)
+    if s.shape != (nb, K // TILE):
+        raise ValueError("scale grid does not match the weight")
+    qt = np.zeros((K, nb * TILE), dtype=np.uint8)
+    qt[:, :N] = q.T
+    return qt, np.ascontiguousarray(s.T)
