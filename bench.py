@@ -62,6 +62,39 @@ def time_events(fn, iters, warmup=3):
     return float(np.mean([s.elapsed_time(e) for s, e in zip(start, end)])) * 1e3
 
 
+def time_graph(fn, calls=20, reps=5):
+    """Average device time of fn() in microseconds, from a HIP graph of
+    `calls` consecutive calls replayed `reps` times between two events (no
+    host launch overhead between kernels).  Falls back to per-call events
+    if the calls cannot be captured."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(calls):
+                    fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+    except Exception:
+        return time_events(fn, calls), "events"
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (calls * reps)
+    del g
+    return us, "graph"
+
+
 def rotation(bytes_per_set, min_total=1 << 29):
     return int(max(1, -(-min_total // max(bytes_per_set, 1))))
 
@@ -77,14 +110,14 @@ def extra_kernels(fb, synth):
     xs = [x0] + [x0.clone() for _ in range(R - 1)]
     qs = [fb.quantize_1x128(x) for x in xs]
     it = iter(range(10 ** 9))
-    us = time_events(lambda: fb.quantize_1x128(xs[next(it) % R]), 30)
+    us, how = time_graph(lambda: fb.quantize_1x128(xs[next(it) % R]))
     byt = 2 * M * K + M * K + 4 * M * (K // 128)
-    out["quantize_1x128_8192x7168"] = dict(us=us, GBs=byt / us / 1e3, frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS,
+    out["quantize_1x128_8192x7168"] = dict(us=us, timing=how, GBs=byt / us / 1e3, frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS,
                                            bytes=byt)
     it = iter(range(10 ** 9))
-    us = time_events(lambda: fb.quantize_transpose_128x1(*qs[next(it) % R]), 30)
+    us, how = time_graph(lambda: fb.quantize_transpose_128x1(*qs[next(it) % R]))
     byt = 2 * M * K + 4 * (M * K // 128) * 2
-    out["quantize_transpose_128x1_8192x7168"] = dict(us=us, GBs=byt / us / 1e3,
+    out["quantize_transpose_128x1_8192x7168"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
                                                      frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
     del xs, qs, x0
     torch.cuda.empty_cache()
@@ -98,13 +131,13 @@ def extra_kernels(fb, synth):
     R = rotation(N * K)
     bsets = [fb.quantize_128x128(wb, pow2=True) for _ in range(R)]
     it = iter(range(10 ** 9))
-    us = time_events(lambda: fb.gemm(a, sa, *bsets[next(it) % R]), 30)
+    us, how = time_graph(lambda: fb.gemm(a, sa, *bsets[next(it) % R]))
     byt = M * K + N * K + 2 * M * N + 4 * (M * K // 128) + 4 * (N // 128) * (K // 128)
-    out["gemm_decode_128x24576x1536_pow2"] = dict(us=us, TFLOPs=2 * M * N * K / us / 1e6,
+    out["gemm_decode_128x24576x1536_pow2"] = dict(us=us, timing=how, TFLOPs=2 * M * N * K / us / 1e6,
                                                   GBs=byt / us / 1e3, frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS,
                                                   bytes=byt)
-    us = time_events(lambda: fb.quantize_1x128(xa, pow2=True), 30)
-    out["quantize_1x128_128x1536_pow2"] = dict(us=us, GBs=(3 * M * K + 4 * M * K // 128) / us / 1e3)
+    us, how = time_graph(lambda: fb.quantize_1x128(xa, pow2=True))
+    out["quantize_1x128_128x1536_pow2"] = dict(us=us, timing=how, GBs=(3 * M * K + 4 * M * K // 128) / us / 1e3)
     del bsets, wb
     torch.cuda.empty_cache()
 
@@ -114,8 +147,8 @@ def extra_kernels(fb, synth):
     a, sa = fb.quantize_1x128(dev_bf16(w["a"]))
     b, sb = fb.quantize_128x128(dev_bf16(w["b"]))
     offs = torch.from_numpy(w["m_offsets"]).cuda()
-    us = time_events(lambda: fb.grouped_gemm_contiguous(a, sa, b, sb, offs), 20)
-    out["grouped_contiguous_8x8192x4096x7168"] = dict(us=us, TFLOPs=2 * Mt * N * K / us / 1e6,
+    us, how = time_graph(lambda: fb.grouped_gemm_contiguous(a, sa, b, sb, offs))
+    out["grouped_contiguous_8x8192x4096x7168"] = dict(us=us, timing=how, TFLOPs=2 * Mt * N * K / us / 1e6,
                                                       frac_mfma=2 * Mt * N * K / us / 1e6 / FP8_PEAK_TFLOPS)
     del a, sa, b, sb
     torch.cuda.empty_cache()
@@ -134,9 +167,43 @@ def extra_kernels(fb, synth):
     flops = 2 * int(c.sum()) * N * K
     nz = int((c > 0).sum())
     byt = nz * (N * K + 4 * (N // 128) * (K // 128)) + int(c.sum()) * (K + 4 * K // 128 + 2 * N)
-    us = time_events(lambda: fb.grouped_gemm_masked(a, sa, b, sb, cnt), 20)
-    out["grouped_masked_32x256x7168x2048"] = dict(us=us, TFLOPs=flops / us / 1e6, GBs=byt / us / 1e3,
+    us, how = time_graph(lambda: fb.grouped_gemm_masked(a, sa, b, sb, cnt))
+    out["grouped_masked_32x256x7168x2048"] = dict(us=us, timing=how, TFLOPs=flops / us / 1e6, GBs=byt / us / 1e3,
                                                   frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
+
+    # backward of the 7168 -> 2112 projection over 4096 tokens: weight
+    # transposed for the data gradient, dX = dY W (K padded 2112 -> 2176), and
+    # the weight gradient dW = dY^T X from the transposed activations
+    T, NO, NI = 4096, 2112, 7168
+    w = synth.dense(T, NO, NI, seed=0)
+    wq, ws = fb.quantize_128x128(dev_bf16(w["b"]))
+    R = rotation(2 * NO * NI)
+    wsets = [(wq.clone(), ws.clone()) for _ in range(R)]
+    it = iter(range(10 ** 9))
+    us, how = time_graph(lambda: fb.transpose_128x128(*wsets[next(it) % R]))
+    NB = (NO + 127) // 128
+    byt = NO * NI + NI * NB * 128 + 2 * 4 * NB * (NI // 128)
+    out["transpose_128x128_2112x7168"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
+                                              frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
+    del wsets
+    qt, st = fb.transpose_128x128(wq, ws)
+    dy_bits = synth.activation(T, NO, seed=1)["a"]
+    pad = np.zeros((T, NB * 128), np.uint16)
+    pad[:, :NO] = dy_bits
+    a, sa = fb.quantize_1x128(dev_bf16(pad))
+    us, how = time_graph(lambda: fb.gemm(a, sa, qt, st))
+    out["gemm_dgrad_4096x7168x2112"] = dict(us=us, timing=how, TFLOPs=2 * T * NI * NO / us / 1e6,
+                                            frac_mfma=2 * T * NI * NO / us / 1e6 / FP8_PEAK_TFLOPS,
+                                            padded_K=NB * 128)
+    x_bits = synth.activation(T, NI, seed=2)["a"]
+    ayt, sayt = fb.quantize_transpose_128x1(a, sa)               # dY^T [Np][T] (zero rows past 2112)
+    axt, saxt = fb.quantize_transpose_128x1(*fb.quantize_1x128(dev_bf16(x_bits)))   # X^T [NI][T]
+    del qt, st, a, sa
+    dw = torch.empty((ayt.shape[0], NI), dtype=torch.float32, device="cuda")
+    us, how = time_graph(lambda: fb.gemm_wgrad(ayt, sayt, axt, saxt, out=dw))
+    Mw = ayt.shape[0]
+    out["gemm_wgrad_2176x7168x4096"] = dict(us=us, timing=how, TFLOPs=2 * Mw * NI * T / us / 1e6,
+                                            frac_mfma=2 * Mw * NI * T / us / 1e6 / FP8_PEAK_TFLOPS)
     return out
 
 

@@ -96,6 +96,20 @@ fp8bs_status fp8bs_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t
   return launched(fp8bs::launch_quantize_128x128(w, G, N, K, q, s, flags & FP8BS_SCALE_POW2, (hipStream_t)stream));
 }
 
+fp8bs_status fp8bs_transpose_128x128(const uint8_t* q, const float* s, int64_t G, int64_t N, int64_t K, uint8_t* qt,
+                                    float* st, fp8bs_stream_t stream) {
+  if (G < 0 || N < 0 || N % 16 || K < 0 || K % 128) return FP8BS_ERR_SHAPE;
+  if (G > kMaxGridY || K / 128 > kMaxGridY) return FP8BS_ERR_SHAPE;
+  if (G == 0 || N == 0 || K == 0) return FP8BS_OK;
+  if (!q || !s || !qt || !st) return FP8BS_ERR_NULL;
+  if (!aligned16(q) || !aligned16(qt) || (reinterpret_cast<uintptr_t>(s) & 3u) ||
+      (reinterpret_cast<uintptr_t>(st) & 3u))
+    return FP8BS_ERR_ALIGN;
+  if (fp8bs_status e = check_device()) return e;
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_transpose_128x128(q, s, G, N, K, qt, st, (hipStream_t)stream));
+}
+
 namespace {
 
 fp8bs_status gemm_common(int64_t N, int64_t K, int32_t out_dtype) {

@@ -205,6 +205,55 @@ __global__ __launch_bounds__(256) void k_quantize_t128x1(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Transposed block-scaled weight (data gradient; page 2, paragraph on
+// hardware suggestions, asks for GEMMs on transposed operands).  W^T keeps
+// W's codes and takes the transposed scale grid; rows of W past N become
+// zero columns up to the next multiple of 128.  One workgroup per 128x128
+// block (x = row block of W, y = column block, z = matrix): the block is
+// staged in LDS in the transpose-requantize layout above, then lane (rg, c4)
+// gathers rows 16*rg .. 16*rg+15 of columns 4*c4 .. 4*c4+3 and writes them
+// as 16 contiguous bytes of four rows of W^T (eight lanes per 128-byte line).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_transpose_128x128(const uint8_t* __restrict__ q, const float* __restrict__ s,
+                                                           int64_t N, int64_t K, uint8_t* __restrict__ qt,
+                                                           float* __restrict__ st) {
+  __shared__ __attribute__((aligned(16))) uint8_t codes[129 * 128];
+  const int64_t nb = blockIdx.x, kb = blockIdx.y, g = blockIdx.z;
+  const int64_t NB = (N + 127) / 128, KT = K / 128, Np = NB * 128;
+  const int t = threadIdx.x;
+  {
+    const int seg = t & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * i + (t >> 3);
+      const int64_t row = nb * 128 + r;
+      const uint4 v = row < N ? nt_load16(q + (g * N + row) * K + kb * 128 + seg * 16) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(codes + t_row(r) * 128 + 16 * (seg ^ (t_swz(r) >> 2))) = v;
+    }
+  }
+  __syncthreads();
+  const int l = t & 63, w = t >> 6;
+  const int rg = l & 7, c4 = 8 * w + (l >> 3);
+  uint32_t wv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 16 * rg + i;
+    wv[i] = *reinterpret_cast<const uint32_t*>(codes + t_row(r) * 128 + 4 * (c4 ^ t_swz(r)));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t packed[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      packed[k] = ((wv[4 * k] >> (8 * j)) & 0xFFu) | (((wv[4 * k + 1] >> (8 * j)) & 0xFFu) << 8) |
+                  (((wv[4 * k + 2] >> (8 * j)) & 0xFFu) << 16) | (((wv[4 * k + 3] >> (8 * j)) & 0xFFu) << 24);
+    nt_store16(qt + (g * K + kb * 128 + 4 * c4 + j) * Np + nb * 128 + 16 * rg,
+               make_uint4(packed[0], packed[1], packed[2], packed[3]));
+  }
+  if (t == 0) st[(g * KT + kb) * NB + nb] = s[(g * NB + nb) * KT + kb];
+}
+
+// ---------------------------------------------------------------------------
 // 128x128 weight blocks.  One workgroup per block (z = matrix, x = row block,
 // y = column block); each lane owns half a row (64 BF16 = 8 loads).  Block
 // amax: DPP row max, then across the 4 DPP rows of a wave and the 4 waves
@@ -317,6 +366,13 @@ hipError_t launch_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t 
     hipLaunchKernelGGL(k_quantize_128x128<true>, grid, dim3(256), 0, stream, (const uint16_t*)w, N, K, q, s);
   else
     hipLaunchKernelGGL(k_quantize_128x128<false>, grid, dim3(256), 0, stream, (const uint16_t*)w, N, K, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_128x128(const uint8_t* q, const float* s, int64_t G, int64_t N, int64_t K, uint8_t* qt,
+                                   float* st, hipStream_t stream) {
+  dim3 grid((unsigned)((N + 127) / 128), (unsigned)(K / 128), (unsigned)G);
+  hipLaunchKernelGGL(k_transpose_128x128, grid, dim3(256), 0, stream, q, s, N, K, qt, st);
   return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ _gcont = _sig("fp8bs_grouped_gemm_fp8_contiguous",
 _gmask = _sig("fp8bs_grouped_gemm_fp8_masked",
               [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P])
 _cast = _sig("fp8bs_cast_f32_to_e4m3", [_P, _I64, _P, _P])
+_t128 = _sig("fp8bs_transpose_128x128", [_P, _P, _I64, _I64, _I64, _P, _P, _P])
 _lib.fp8bs_status_str.argtypes = [ctypes.c_int]
 _lib.fp8bs_status_str.restype = ctypes.c_char_p
 _lib.fp8bs_abi_version.argtypes = []
@@ -150,6 +151,28 @@ def quantize_128x128(w: torch.Tensor, pow2: bool = False):
     _check(_q128(_ptr(w), G, N, K, _ptr(q), _ptr(s), SCALE_POW2 if pow2 else 0, _stream(w)),
            "quantize_128x128")
     return q, s
+
+
+def transpose_128x128(q: torch.Tensor, s: torch.Tensor):
+    """Block-scaled weight q[N][K] (or [G][N][K]) with s[ceil(N/128)][K/128]
+    -> the transposed weight (qt[K][Np], st[K/128][Np/128]), Np =
+    128*ceil(N/128), columns past N zero: the B operand of the data gradient
+    dX = dY W (dY quantized over the zero-padded width Np)."""
+    _codes(q, "q")
+    _need(q, "q")
+    if q.dim() not in (2, 3):
+        raise ValueError("q must be [N][K] or [G][N][K]")
+    G, N, K = (1, *q.shape) if q.dim() == 2 else q.shape
+    NB = (N + 127) // 128
+    sshape = (NB, K // 128) if q.dim() == 2 else (G, NB, K // 128)
+    _need(s, "s", torch.float32, len(sshape))
+    if tuple(s.shape) != sshape:
+        raise ValueError("scale grid does not match the weight")
+    qt = torch.empty((K, NB * 128) if q.dim() == 2 else (G, K, NB * 128), dtype=torch.float8_e4m3fn,
+                     device=q.device)
+    st = torch.empty((K // 128, NB) if q.dim() == 2 else (G, K // 128, NB), dtype=torch.float32, device=q.device)
+    _check(_t128(_ptr(q), _ptr(s), G, N, K, _ptr(qt), _ptr(st), _stream(q)), "transpose_128x128")
+    return qt, st
 
 
 def gemm(a, sa, b, sb, out_dtype=torch.bfloat16, out=None):

@@ -129,6 +129,26 @@ fp8bs_status fp8bs_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t
                                     fp8bs_stream_t stream);
 
 /*
+ * Transposed block-scaled weight, for the data gradient dX = dY W (page 2,
+ * "A Deadly Mistake Uncovered on Deepseek China Ai", paragraph on hardware
+ * suggestions: GEMMs on transposed operands).  A 128x128-block-scaled weight
+ * transposed is again block-scaled, with the same codes and the transposed
+ * scale grid; nothing is requantized.  Rows of W past N become zero columns
+ * up to Np = 128 * ceil(N/128), so the result is a GEMM weight operand with
+ * K' = Np (quantize the activation gradient over the same zero-padded width).
+ *   q  : E4M3 [G][N][K],   s  : FP32 [G][ceil(N/128)][K/128]   (input)
+ *   qt : E4M3 [G][K][Np],  st : FP32 [G][K/128][Np/128]        (output;
+ *        qt[g][k][n] = q[g][n][k] for n < N, 0 otherwise;
+ *        st[g][kb][nb] = s[g][nb][kb])
+ * Requires G >= 0, N >= 0, N % 16 == 0, K >= 0, K % 128 == 0; q and qt
+ * 16-byte aligned, s and st 4-byte aligned.
+ */
+fp8bs_status fp8bs_transpose_128x128(const uint8_t* q, const float* s,
+                                     int64_t G, int64_t N, int64_t K,
+                                     uint8_t* qt, float* st,
+                                     fp8bs_stream_t stream);
+
+/*
  * Dense block-scaled FP8 GEMM (page 1, paragraphs on FP8 GEMM inputs/outputs
  * and FP32 promotion; page 4, section "Schluesselmerkmale von DeepGemm",
  * dense layout).  D = A * B^T.
