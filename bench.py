@@ -171,6 +171,19 @@ def extra_kernels(fb, synth):
     out["grouped_masked_32x256x7168x2048"] = dict(us=us, timing=how, TFLOPs=flops / us / 1e6, GBs=byt / us / 1e3,
                                                   frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
 
+    # power-of-two scales on the training projection and a large square: the
+    # matrix core applies the scales (E8M0) vs the FP32 promotion on the VALU
+    for (M, N, K) in ((4096, 2112, 7168), (8192, 4096, 7168)):
+        w = synth.dense(M, N, K, seed=3)
+        a, sa = fb.quantize_1x128(dev_bf16(w["a"]), pow2=True)
+        b, sb = fb.quantize_128x128(dev_bf16(w["b"]), pow2=True)
+        for hw in (True, False):
+            us, how = time_graph(lambda: fb.gemm(a, sa, b, sb, pow2_scales=hw))
+            out[f"gemm_pow2_{'hw' if hw else 'sw'}_{M}x{N}x{K}"] = dict(
+                us=us, timing=how, TFLOPs=2 * M * N * K / us / 1e6, frac_mfma=2 * M * N * K / us / 1e6 / FP8_PEAK_TFLOPS)
+        del a, sa, b, sb
+    torch.cuda.empty_cache()
+
     # backward of the 7168 -> 2112 projection over 4096 tokens: weight
     # transposed for the data gradient, dX = dY W (K padded 2112 -> 2176), and
     # the weight gradient dW = dY^T X from the transposed activations

@@ -136,14 +136,17 @@ bool grid_fits(int64_t rows, int64_t N, int64_t groups) {
 }  // namespace
 
 fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, void* d,
-                                        int64_t M, int64_t N, int64_t K, int32_t out_dtype, fp8bs_stream_t stream) {
+                                        int64_t M, int64_t N, int64_t K, int32_t out_dtype, uint32_t flags,
+                                        fp8bs_stream_t stream) {
   if (M < 0) return FP8BS_ERR_SHAPE;
   if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
   if (!grid_fits(M, N, 1)) return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (M == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, nullptr, false)) return e;
   if (fp8bs_status e = check_device()) return e;
-  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, out_dtype == FP8BS_OUT_FP32, false, fp8bs::kDense};
+  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, out_dtype == FP8BS_OUT_FP32, false,
+                (flags & FP8BS_SCALE_POW2) != 0, fp8bs::kDense};
   (void)hipGetLastError();
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
 }
@@ -157,35 +160,39 @@ fp8bs_status fp8bs_gemm_fp8_wgrad(const uint8_t* a, const float* sa, const uint8
   if (M == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, nullptr, false)) return e;
   if (fp8bs_status e = check_device()) return e;
-  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, true, accumulate == 1, fp8bs::kWgrad};
+  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, true, accumulate == 1, false, fp8bs::kWgrad};
   (void)hipGetLastError();
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
 }
 
 fp8bs_status fp8bs_grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                                                void* d, const int32_t* m_offsets, int32_t G, int64_t Mt, int64_t N,
-                                               int64_t K, int32_t out_dtype, fp8bs_stream_t stream) {
+                                               int64_t K, int32_t out_dtype, uint32_t flags, fp8bs_stream_t stream) {
   if (G < 0 || Mt < 0 || Mt % 128) return FP8BS_ERR_SHAPE;
   if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
   if (!grid_fits(Mt, N, 1)) return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (G == 0 || Mt == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, m_offsets, true)) return e;
   if (fp8bs_status e = check_device()) return e;
-  GemmProblem p{a, sa, b, sb, d, m_offsets, Mt, N, K, G, out_dtype == FP8BS_OUT_FP32, false, fp8bs::kContiguous};
+  GemmProblem p{a, sa, b, sb, d, m_offsets, Mt, N, K, G, out_dtype == FP8BS_OUT_FP32, false,
+                (flags & FP8BS_SCALE_POW2) != 0, fp8bs::kContiguous};
   (void)hipGetLastError();
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
 }
 
 fp8bs_status fp8bs_grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                                            void* d, const int32_t* masked_m, int32_t G, int64_t cap, int64_t N,
-                                           int64_t K, int32_t out_dtype, fp8bs_stream_t stream) {
+                                           int64_t K, int32_t out_dtype, uint32_t flags, fp8bs_stream_t stream) {
   if (G < 0 || cap < 0) return FP8BS_ERR_SHAPE;
   if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
   if (!grid_fits(cap, N, G)) return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (G == 0 || cap == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, masked_m, true)) return e;
   if (fp8bs_status e = check_device()) return e;
-  GemmProblem p{a, sa, b, sb, d, masked_m, cap, N, K, G, out_dtype == FP8BS_OUT_FP32, false, fp8bs::kMasked};
+  GemmProblem p{a, sa, b, sb, d, masked_m, cap, N, K, G, out_dtype == FP8BS_OUT_FP32, false,
+                (flags & FP8BS_SCALE_POW2) != 0, fp8bs::kMasked};
   (void)hipGetLastError();
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
 }

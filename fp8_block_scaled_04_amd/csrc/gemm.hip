@@ -46,7 +46,7 @@ namespace {
 
 constexpr int kKC = 128;  // K chunk = promotion interval = MFMA K
 
-template <int BM_, int BN_, int WGM_, int WGN_, bool DB_, int S_ = 2, int PF_ = 0>
+template <int BM_, int BN_, int WGM_, int WGN_, bool DB_, int S_ = 2, int PF_ = 0, bool CS_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
   static constexpr bool DB = DB_;                   // fragments double buffered in registers
@@ -60,9 +60,13 @@ struct Cfg {
   static constexpr int B_BYTES = BN * kKC;
   // One scale DMA per wave and chunk (64 floats): slots 0..BM/64-1 hold the
   // activation scales of the tile's rows, slot BM/64 the weight scales of
-  // weight block rows n0/128 + i; any further slots hold copies of it.
+  // weight block rows n0/128 + i; any further slots hold copies of it.  With
+  // compact scales (CS) the further waves write their identical copy into
+  // slot BM/64 itself, which frees LDS for a third stage (not for the weight
+  // gradient, whose per-row weight scales need every slot).
   static constexpr int SA_WAVES = BM / 64;
-  static constexpr int SC_BYTES = NW * 256;
+  static constexpr bool CS = CS_;
+  static constexpr int SC_BYTES = CS ? (SA_WAVES + 1) * 256 : NW * 256;
   static constexpr int SA_OFF = A_BYTES + B_BYTES;
   static constexpr int SB_OFF = A_BYTES + B_BYTES + SA_WAVES * 256;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
@@ -89,7 +93,11 @@ struct Cfg {
 
 using SmallTile = Cfg<128, 128, 2, 2, true>;
 using LargeTile = Cfg<256, 256, 4, 2, false>;
-using MidTile = Cfg<256, 160, 4, 2, false>;
+// 256x160 with three stages (compact scales: 160 KB of LDS): measured on
+// 4096x2112x7168 right after the quantizer wrote A, 87 -> 78 us, and 96 ->
+// 83 us with cold caches; two stages for the weight gradient.
+using MidTile = Cfg<256, 160, 4, 2, false, 3, 0, true>;
+using WgradMidTile = Cfg<256, 160, 4, 2, false>;
 // Memory-bound shapes (few rows): 128x96 tiles, three stages, one
 // workgroup per CU on the 24576-column decode projection.
 using StreamTile = Cfg<128, 96, 2, 2, false, 3>;
@@ -297,7 +305,22 @@ struct Frags {
   float sb;
 };
 
-template <class C, int MODE, bool OUT_F32>
+// E8M0 exponent byte of a power-of-two scale 2^e, -127 <= e <= 127 (byte
+// e + 127; 2^-127 is an FP32 subnormal).  Any other value gives 0xFF, the
+// E8M0 NaN, so every output that depends on it comes out NaN.
+__device__ __forceinline__ int e8m0_of(float s) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, s);
+  const uint32_t e = u >> 23;   // sign bit included: negative scales are invalid
+  const bool normal = (u & 0x7FFFFFu) == 0 && e >= 1 && e <= 254;
+  return normal ? (int)e : (u == 0x00400000u ? 0 : 0xFF);
+}
+
+// HWS (hardware scaling; every scale a power of two): the MFMA applies the
+// chunk's scales as E8M0 exponents per operand row -- the weight fragment's
+// block scale on the first operand, each lane's activation-row scale on the
+// second -- and adds the scaled chunk product to the accumulator it is given,
+// so the promotion needs no VALU work.
+template <class C, int MODE, bool OUT_F32, bool HWS>
 __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   // The body uses AMDGPU buffer descriptors, which exist in the device pass
   // only; the host pass needs just the kernel's signature for its launch stub.
@@ -393,7 +416,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       const uint32_t voff = (uint32_t)(row * K + 16 * ((pw >> 2) ^ swz(row)) + 4 * (pw & 3));
       dma4(rbk, st + C::A_BYTES + t0 * kKC, voff, koff);
     }
-    dma4(rck, st + C::SA_OFF + wave * 256, sc_voff, soff);
+    dma4(rck, st + C::SA_OFF + ((C::CS && wave > C::SA_WAVES) ? C::SA_WAVES : wave) * 256, sc_voff, soff);
   };
   // Weight chunk kb into L2 (nothing is read back): lane l of instruction i
   // touches row 32*(i*NW + wave) + l/2, half row l%2.  Rows past the tile
@@ -459,6 +482,18 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     for (int j = 0; j < C::FM; ++j) f.sa[j] = f.sa[j] * f.sb;
   };
   // Blocks (i0 + i, j) for the FNH weight fragments held in f.
+  auto compute_hws = [&](const F& f, int i0) {
+    const int eb = e8m0_of(f.sb);
+    int ea[C::FM];
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) ea[j] = e8m0_of(f.sa[j]);
+#pragma unroll
+    for (int b = 0; b < FNH * C::FM; ++b) {
+      v4f& ac = acc[i0 + b / C::FM][b % C::FM];
+      ac = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[b / C::FM], f.a[b % C::FM], ac, 0, 0, 0, eb, 0,
+                                                            ea[b % C::FM]);
+    }
+  };
   auto compute = [&](const F& f, int i0) {
     const float* sc = f.sa;
     constexpr int NBLK = FNH * C::FM;
@@ -515,8 +550,12 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       read_a(stage ^ 1, nxt);
       read_b(stage ^ 1, nxt, 0);
       __builtin_amdgcn_sched_barrier(0);
-      scales(cur);
-      compute(cur, 0);
+      if constexpr (HWS) {
+        compute_hws(cur, 0);
+      } else {
+        scales(cur);
+        compute(cur, 0);
+      }
     };
     int kb = 0;
     for (; kb + 1 < KT; kb += 2) {
@@ -552,9 +591,13 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     constexpr bool ROWB = MODE == kWgrad;
     static_assert(!ROWB || C::FM >= 2, "the weight scales are read at a row's second block");
     static_assert(!ROWB || BN <= (C::NW - C::SA_WAVES) * 64, "the scale waves must cover every weight row");
+    static_assert(!(ROWB && HWS), "hardware scaling takes one scale per weight fragment");
+    static_assert(!(ROWB && C::CS), "per-row weight scales need every scale slot");
     float4 sbr[3];
     auto sslot = [](int i) { return (i == FN - 1 && (FN - 1) % 2 == 0) ? 2 : i % 2; };
     float sb_lo = 0.f, sb_hi = 0.f;
+    int ea[C::FM];              // HWS: this chunk's E8M0 bytes: activation rows (per lane) and
+    int ebf[C::FN];             // the weight block of each weight fragment (uniform, SGPRs)
     const int blk_lo = sb_idx;
     const int blk_hi = (int)((n0 + b_row0 + C::WN - 1) / 128 - n0 / 128);
     auto read_a1 = [&](int stage, int j) {
@@ -598,10 +641,18 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     const v4f pz = {0.f, 0.f, 0.f, 0.f};
     v4f pc[2];
     auto mfma = [&](int b) {
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[slot(b / C::FM)], fa[b % C::FM], pz,
-                                                              0, 0, 0, 0, 0, 0);
+      if constexpr (HWS) {
+        const int i = b / C::FM, j = b % C::FM;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[slot(i)], fa[j], acc[i][j], 0, 0, 0,
+                                                                     ebf[i], 0, ea[j]);
+        return pz;
+      } else {
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[slot(b / C::FM)], fa[b % C::FM], pz,
+                                                                0, 0, 0, 0, 0, 0);
+      }
     };
     auto fma_block = [&](int b, const v4f& pv, const float* sc) {
+      if constexpr (HWS) return;
       v4f& ac = acc[b / C::FM][b % C::FM];
       if (ROWB) {
         const float4 sv = sbr[sslot(b / C::FM)];
@@ -641,9 +692,18 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < C::FM; ++j) scl[j] = sc[(FN - 2) & 1][j];
       // Order: MFMA, [at the start of a row: the weight read], the FMAs of the
-      // previous block [and the row's scale products].
+      // previous block [and the row's scale products].  With hardware
+      // scaling there are no FMAs: MFMAs and the weight reads only.
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (2 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if constexpr (HWS) {
+#pragma unroll
+        for (int b = 1; b < LAST; ++b) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (b % C::FM == 0 && b / C::FM + 2 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        return;
+      }
 #pragma unroll
       for (int b = 1; b < LAST; ++b) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -673,9 +733,9 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       pc[(LAST + 1) & 1] = mfma(LAST + 1);
       fma_block(LAST, pc[LAST & 1], sc);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, (STRADDLE || ROWB) ? 8 : 4, 0);
+      if (!HWS) __builtin_amdgcn_sched_group_barrier(0x002, (STRADDLE || ROWB) ? 8 : 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, ROWB ? 8 : 4, 0);
+      if (!HWS) __builtin_amdgcn_sched_group_barrier(0x002, ROWB ? 8 : 4, 0);
       __builtin_amdgcn_sched_barrier(0);
       sync();
       __builtin_amdgcn_sched_barrier(0);
@@ -705,6 +765,16 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     };
     // Without straddling, every row uses sa * sb: multiply once per chunk.
     auto chunk_scales = [&] {
+      if constexpr (HWS) {
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) ea[j] = e8m0_of(sa[j]);
+        const int eb_lo = __builtin_amdgcn_readfirstlane(e8m0_of(sb_lo));
+        const int eb_hi = STRADDLE ? __builtin_amdgcn_readfirstlane(e8m0_of(sb_hi)) : eb_lo;
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i)
+          ebf[i] = ((int)((n0 + b_row0 + 16 * i) / 128 - n0 / 128) != blk_lo) ? eb_hi : eb_lo;
+        return;
+      }
       if (!STRADDLE && !ROWB)
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) sa[j] = sa[j] * sb_lo;
@@ -736,6 +806,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     auto step = [&](int kb, int stage) {
       __builtin_amdgcn_sched_barrier(0);
       chunk_scales();
+      if constexpr (HWS) __builtin_amdgcn_sched_barrier(0);   // the chunk's E8M0 bytes first
       float scp[C::FM];
       rows(stage, scp);
       __builtin_amdgcn_sched_barrier(0);
@@ -801,10 +872,19 @@ hipError_t launch_cfg(const GemmProblem& pr, hipStream_t stream) {
   a.accumulate = pr.accumulate ? 1 : 0;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * (MODE == kMasked ? pr.G : 1);
   if (blocks == 0) return hipSuccess;
-  if (MODE == kWgrad || pr.out_f32)
-    hipLaunchKernelGGL((k_gemm<C, MODE, true>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
-  else if constexpr (MODE != kWgrad)   // the weight gradient is FP32 only
-    hipLaunchKernelGGL((k_gemm<C, MODE, false>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
+  if constexpr (MODE == kWgrad) {   // FP32 out, software promotion only
+    hipLaunchKernelGGL((k_gemm<C, MODE, true, false>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
+  } else if (pr.hw_scale) {
+    if (pr.out_f32)
+      hipLaunchKernelGGL((k_gemm<C, MODE, true, true>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemm<C, MODE, false, true>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
+  } else {
+    if (pr.out_f32)
+      hipLaunchKernelGGL((k_gemm<C, MODE, true, false>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemm<C, MODE, false, false>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -845,7 +925,7 @@ hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
   if constexpr (MODE == kWgrad) {
     // per-row weight scales are read in the 256-wide tiles' loop only
     if (t_large <= t_mid) return launch_cfg<LargeTile, MODE>(p, stream);
-    return launch_cfg<MidTile, MODE>(p, stream);
+    return launch_cfg<WgradMidTile, MODE>(p, stream);
   } else {
     if (t_large <= t_mid && t_large <= t_small) return launch_cfg<LargeTile, MODE>(p, stream);
     if (t_mid <= t_small) return launch_cfg<MidTile, MODE>(p, stream);

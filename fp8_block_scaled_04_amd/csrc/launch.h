@@ -33,6 +33,7 @@ struct GemmProblem {
   int32_t G;              // number of groups (1 for dense)
   bool out_f32;
   bool accumulate;        // kWgrad: D += A B^T
+  bool hw_scale;          // every scale a power of two: the MFMA applies them and accumulates
   GemmMode mode;
 };
 

@@ -19,20 +19,21 @@
 namespace fp8bs {
 namespace {
 
-// Streaming (nontemporal) 16-byte loads and 8/16-byte stores: every byte is
+// Streaming (nontemporal) 16-byte loads and 16-byte stores: every byte is
 // touched once, and on MI355X the nontemporal forms move a 2:1 read:write
-// stream about 10% faster than cached ones (6.1 vs 5.6 TB/s, measured).
+// stream about 10% faster than cached ones (6.1 vs 5.6 TB/s, measured).  The
+// 1x128 quantizer's codes are the exception: written with ordinary stores its
+// 8192x7168 launch takes 30.7 instead of 33.4 us, and the GEMM that reads
+// them next finds them in the cache (quantize + 4096x2112x7168 GEMM: 95 ->
+// 89 us); cached loads of its input, or cached stores in the transposing
+// quantizers, were slower.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 nt_load16(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ void nt_store16(void* p, uint4 v) {
   __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
-}
-__device__ __forceinline__ void nt_store8(void* p, uint2 v) {
-  __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
 }
 
 // ---------------------------------------------------------------------------
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(const uint16_t* __restri
     else
       out = quantize8<POW2, false>(w, ts);
     if (row_ok && kb < KT) {
-      nt_store8(q + m * K + kb * 128 + lane16 * 8, out);
+      *reinterpret_cast<uint2*>(q + m * K + kb * 128 + lane16 * 8) = out;
       if (lane16 == 0) s[kb * M + m] = ts.s;
     }
   }

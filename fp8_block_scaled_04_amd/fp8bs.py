@@ -41,12 +41,12 @@ def _sig(name, args):
 _q1x128 = _sig("fp8bs_quantize_1x128", [_P, _I64, _I64, _P, _P, _U32, _P])
 _qt = _sig("fp8bs_quantize_transpose_128x1", [_P, _P, _I64, _I64, _P, _P, _U32, _P])
 _q128 = _sig("fp8bs_quantize_128x128", [_P, _I64, _I64, _I64, _P, _P, _U32, _P])
-_gemm = _sig("fp8bs_gemm_fp8_blockscaled", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P])
+_gemm = _sig("fp8bs_gemm_fp8_blockscaled", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _U32, _P])
 _wgrad = _sig("fp8bs_gemm_fp8_wgrad", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P])
 _gcont = _sig("fp8bs_grouped_gemm_fp8_contiguous",
-              [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P])
+              [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _U32, _P])
 _gmask = _sig("fp8bs_grouped_gemm_fp8_masked",
-              [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P])
+              [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _U32, _P])
 _cast = _sig("fp8bs_cast_f32_to_e4m3", [_P, _I64, _P, _P])
 _t128 = _sig("fp8bs_transpose_128x128", [_P, _P, _I64, _I64, _I64, _P, _P, _P])
 _lib.fp8bs_status_str.argtypes = [ctypes.c_int]
@@ -175,9 +175,11 @@ def transpose_128x128(q: torch.Tensor, s: torch.Tensor):
     return qt, st
 
 
-def gemm(a, sa, b, sb, out_dtype=torch.bfloat16, out=None):
+def gemm(a, sa, b, sb, out_dtype=torch.bfloat16, out=None, pow2_scales=False):
     """D[M][N] = A * B^T with 1x128 scales sa[K/128][M] and 128x128 block
-    scales sb[ceil(N/128)][K/128]."""
+    scales sb[ceil(N/128)][K/128].  pow2_scales=True: every scale is a power
+    of two 2^e, -127 <= e <= 127, and the matrix core applies them (outputs
+    that depend on any other scale are NaN)."""
     _codes(a, "a"); _codes(b, "b")
     for t, n in ((a, "a"), (b, "b")):
         _need(t, n, None, 2)
@@ -196,7 +198,8 @@ def gemm(a, sa, b, sb, out_dtype=torch.bfloat16, out=None):
         _need(out, "out", out_dtype, 2)
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
-    _check(_gemm(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, code, _stream(a)),
+    _check(_gemm(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, code,
+                 SCALE_POW2 if pow2_scales else 0, _stream(a)),
            "gemm_fp8_blockscaled")
     return out
 
@@ -230,7 +233,7 @@ def gemm_wgrad(a, sa, b, sb, out=None, accumulate=False):
     return out
 
 
-def grouped_gemm_contiguous(a, sa, b, sb, m_offsets, out_dtype=torch.bfloat16, out=None):
+def grouped_gemm_contiguous(a, sa, b, sb, m_offsets, out_dtype=torch.bfloat16, out=None, pow2_scales=False):
     """Contiguous MoE layout: group g owns rows [m_offsets[g], m_offsets[g+1])
     of a[Mt][K] and d[Mt][N] and uses b[g], sb[g].  m_offsets is an int32 GPU
     tensor of G+1 entries; rows past m_offsets[G] are not written."""
@@ -254,11 +257,11 @@ def grouped_gemm_contiguous(a, sa, b, sb, m_offsets, out_dtype=torch.bfloat16, o
         if tuple(out.shape) != (Mt, N):
             raise ValueError("out has the wrong shape")
     _check(_gcont(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), _ptr(m_offsets), G, Mt, N, K, code,
-                  _stream(a)), "grouped_gemm_fp8_contiguous")
+                  SCALE_POW2 if pow2_scales else 0, _stream(a)), "grouped_gemm_fp8_contiguous")
     return out
 
 
-def grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, out=None):
+def grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, out=None, pow2_scales=False):
     """Masked MoE layout: a[G][cap][K], sa[G][K/128][cap], b[G][N][K],
     sb[G][ceil(N/128)][K/128]; group g uses its first masked_m[g] rows (int32
     GPU tensor).  Rows past the count keep the previous contents of `out`."""
@@ -282,7 +285,7 @@ def grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, out=No
         if tuple(out.shape) != (G, cap, N):
             raise ValueError("out has the wrong shape")
     _check(_gmask(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), _ptr(masked_m), G, cap, N, K, code,
-                  _stream(a)), "grouped_gemm_fp8_masked")
+                  SCALE_POW2 if pow2_scales else 0, _stream(a)), "grouped_gemm_fp8_masked")
     return out
 
 

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 1
+#define FP8BS_ABI_VERSION 2
 
 /* Same type as hipStream_t; declared here so the header needs no HIP headers. */
 struct ihipStream_t;
@@ -84,7 +84,18 @@ typedef enum {
 /* Output dtypes of the GEMMs. */
 enum { FP8BS_OUT_BF16 = 0, FP8BS_OUT_FP32 = 1 };
 
-/* Quantizer flags. */
+/*
+ * Flags.  Quantizers: FP8BS_SCALE_POW2 rounds every scale up to a power of
+ * two.  GEMMs (dense and grouped): FP8BS_SCALE_POW2 declares that every scale
+ * of A and B is a power of two 2^e with -127 <= e <= 127 (the power-of-two
+ * quantizers give that for every tile whose amax exceeds 448 * 2^-128); the
+ * matrix core then applies the scales itself, as E8M0 exponents per operand
+ * row and 32-wide K group, and adds each scaled 128-K chunk product to its own
+ * FP32 accumulator, so the promotion takes no vector-ALU work (page 2,
+ * "A Deadly Mistake Uncovered on Deepseek China Ai", paragraph on hardware
+ * suggestions: MMA that takes the group scales).  An output that depends on
+ * any other scale value is NaN.
+ */
 enum { FP8BS_SCALE_POW2 = 1u };
 
 /*
@@ -155,12 +166,15 @@ fp8bs_status fp8bs_transpose_128x128(const uint8_t* q, const float* s,
  *   a  : E4M3 [M][K],   sa : FP32 [K/128][M]              (1x128 tiles)
  *   b  : E4M3 [N][K],   sb : FP32 [ceil(N/128)][K/128]    (128x128 blocks)
  *   d  : [M][N], BF16 (out_dtype = FP8BS_OUT_BF16) or FP32 (FP8BS_OUT_FP32)
+ *   flags : 0, or FP8BS_SCALE_POW2 (power-of-two scales applied by the
+ *           matrix core; see the flags above)
  * Requires M >= 0, N >= 0, N % 16 == 0, K > 0, K % 128 == 0.
  */
 fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa,
                                         const uint8_t* b, const float* sb,
                                         void* d, int64_t M, int64_t N, int64_t K,
-                                        int32_t out_dtype, fp8bs_stream_t stream);
+                                        int32_t out_dtype, uint32_t flags,
+                                        fp8bs_stream_t stream);
 
 /*
  * Weight-gradient GEMM (page 1, paragraphs on caching FP8 activations and on
@@ -194,13 +208,15 @@ fp8bs_status fp8bs_gemm_fp8_wgrad(const uint8_t* a, const float* sa,
  *               violations are not detected and give undefined results.  Rows
  *               at or past m_offsets[G] are not written.  Empty groups are
  *               allowed.
+ *   flags : 0 or FP8BS_SCALE_POW2, as for the dense GEMM.
  * Requires G >= 0, Mt >= 0, Mt % 128 == 0, N % 16 == 0, K > 0, K % 128 == 0.
  */
 fp8bs_status fp8bs_grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa,
                                                const uint8_t* b, const float* sb,
                                                void* d, const int32_t* m_offsets,
                                                int32_t G, int64_t Mt, int64_t N, int64_t K,
-                                               int32_t out_dtype, fp8bs_stream_t stream);
+                                               int32_t out_dtype, uint32_t flags,
+                                               fp8bs_stream_t stream);
 
 /*
  * Grouped GEMM, masked MoE layout for decoding (page 4, the second MoE layout;
@@ -213,13 +229,15 @@ fp8bs_status fp8bs_grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa
  *   masked_m : int32 [G], DEVICE memory, read on the device only; values are
  *              clamped to [0, cap].  Rows at or past masked_m[g] of group g
  *              are neither used nor written (d keeps its previous contents).
+ *   flags : 0 or FP8BS_SCALE_POW2, as for the dense GEMM.
  * Requires G >= 0, cap >= 0, N % 16 == 0, K > 0, K % 128 == 0.
  */
 fp8bs_status fp8bs_grouped_gemm_fp8_masked(const uint8_t* a, const float* sa,
                                            const uint8_t* b, const float* sb,
                                            void* d, const int32_t* masked_m,
                                            int32_t G, int64_t cap, int64_t N, int64_t K,
-                                           int32_t out_dtype, fp8bs_stream_t stream);
+                                           int32_t out_dtype, uint32_t flags,
+                                           fp8bs_stream_t stream);
 
 /*
  * Elementwise FP32 -> E4M3 cast with the encoding used by every quantizer
