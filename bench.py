@@ -62,14 +62,19 @@ def time_events(fn, iters, warmup=3):
     return float(np.mean([s.elapsed_time(e) for s, e in zip(start, end)])) * 1e3
 
 
+EAGER = False   # --eager: per-kernel lines from plain launches (for profiler runs)
+
+
 def time_graph(fn, calls=20, reps=5):
     """Average device time of fn() in microseconds, from a HIP graph of
     `calls` consecutive calls replayed `reps` times between two events (no
     host launch overhead between kernels).  Falls back to per-call events
-    if the calls cannot be captured."""
+    if the calls cannot be captured, or with --eager."""
     for _ in range(3):
         fn()
     torch.cuda.synchronize()
+    if EAGER:
+        return time_events(fn, calls), "events"
     try:
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
@@ -270,10 +275,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel workload table")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the per-kernel table with plain launches instead of graph replays")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
+    global EAGER
+    EAGER = args.eager
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a single "
               "device: each kernel works on one GPU's share and nothing here communicates)", file=sys.stderr)
