@@ -22,6 +22,14 @@ What they compute, and where it comes from:
   requantization is involved.  Rows of W past the last multiple of 128 (a
   ragged N) become zero columns, so the transposed weight's K is a multiple
   of 128 (the activation gradient is quantized over the same padded width).
+* Both tilings from one read of the BF16 activation: page 2, paragraph on
+  hardware suggestions, asks for the FP8 cast to happen while activations
+  move, so they are not read and written again just to quantize them.  The
+  forward GEMM needs 1x128 tiles and the weight gradient 128x1 tiles
+  (transposed); a single pass over the BF16 values can produce both.  By
+  definition the 128x1 tiles of x are the 1x128 tiles of x^T, quantized from
+  the BF16 values directly (one rounding, unlike the conversion from the
+  cached FP8 copy above).
 * Power-of-two scales: page 2, same paragraph as the 14-bit accumulation
   note, says some activations use scaling factors that are integral powers of
   two.  Read here as: round the FP32 scale UP to the next power of two, so no
@@ -41,6 +49,8 @@ Scale layouts (row-major, M contiguous for activations):
   quantize_1x128            x[R][C]  -> q[R][C],  s[C/128][R]
   quantize_transpose_128x1  q[M][K], s[K/128][M] -> qt[K][M], st[M/128][K]
   quantize_128x128          w[N][K]  -> q[N][K],  s[ceil(N/128)][K/128]
+  quantize_dual             x[M][K]  -> q[M][K], s[K/128][M] (1x128) and
+                                        qt[K][M], st[M/128][K] (128x1, transposed)
   transpose_128x128         q[N][K], s[ceil(N/128)][K/128] -> qt[K][Np], st[K/128][Np/128],
                             Np = 128 * ceil(N/128)
 """
@@ -164,3 +174,17 @@ def transpose_128x128(q, s):
     qt = np.zeros((K, nb * TILE), dtype=np.uint8)
     qt[:, :N] = q.T
     return qt, np.ascontiguousarray(s.T)
+
+
+def quantize_dual(x_bf16_bits, pow2: bool = False):
+    """BF16 x[M][K] (M, K multiples of 128) -> (q, s, qt, st): the 1x128
+    quantization of x and the 128x1 quantization of x stored transposed, both
+    from the BF16 values.  The second is by definition the 1x128 quantization
+    of x^T."""
+    x = np.asarray(x_bf16_bits, dtype=np.uint16)
+    M, K = x.shape
+    if M % TILE or K % TILE:
+        raise ValueError("M and K must be multiples of 128")
+    q, s = quantize_1x128(x, pow2)
+    qt, st = quantize_1x128(np.ascontiguousarray(x.T), pow2)
+    return q, s, qt, st

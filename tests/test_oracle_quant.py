@@ -166,3 +166,25 @@ def test_underflowing_scale_is_clamped_to_smallest_float32():
     q, s = quantize.quantize_rows_f32(x)
     assert s[0, 0] == np.float32(2.0 ** -149) == np.float32(tile_scale_exact(2.0 ** -145, False))
     assert q[0, :4].tolist() == [nearest_code(16.0, TAB), nearest_code(-4.0, TAB), nearest_code(1.0, TAB), 0]
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_dual_quantize_both_tilings(pow2):
+    # 1x128 tiles along rows and 128x1 tiles along columns of the same BF16
+    # values: tile invariants on x and on x^T, and Fraction-exact scale and
+    # codes on sampled columns (an outlier channel makes the column tiles
+    # differ sharply from the row tiles)
+    x = synth.activation(256, 384, seed=11)["a"]
+    q, s, qt, st = quantize.quantize_dual(x, pow2)
+    assert q.shape == (256, 384) and s.shape == (3, 256)
+    assert qt.shape == (384, 256) and st.shape == (2, 384)
+    x32 = bf16.to_f32(x)
+    check_tile_invariants(x32, q, s.T, pow2)
+    check_tile_invariants(np.ascontiguousarray(x32.T), qt, st.T, pow2)
+    for c in (0, 5, 383):
+        for mb in range(2):
+            col = x32[mb * 128:(mb + 1) * 128, c].astype(np.float64)
+            sc = tile_scale_exact(float(np.max(np.abs(col))), pow2)
+            assert st[mb, c] == np.float32(sc)
+            want = [nearest_code(rn32(Fraction(float(v)) / Fraction(sc)), TAB) for v in col]
+            assert np.array_equal(qt[c, mb * 128:(mb + 1) * 128], np.array(want, np.uint8))
