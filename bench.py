@@ -124,6 +124,11 @@ def extra_kernels(fb, synth):
     byt = 2 * M * K + 4 * (M * K // 128) * 2
     out["quantize_transpose_128x1_8192x7168"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
                                                      frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
+    it = iter(range(10 ** 9))
+    us, how = time_graph(lambda: fb.quantize_dual(xs[next(it) % R]))
+    byt = 2 * M * K + 2 * M * K + 8 * (M * K // 128)
+    out["quantize_dual_8192x7168"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
+                                          frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
     del xs, qs, x0
     torch.cuda.empty_cache()
 

@@ -96,6 +96,19 @@ fp8bs_status fp8bs_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t
   return launched(fp8bs::launch_quantize_128x128(w, G, N, K, q, s, flags & FP8BS_SCALE_POW2, (hipStream_t)stream));
 }
 
+fp8bs_status fp8bs_quantize_dual(const void* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt, float* st,
+                                uint32_t flags, fp8bs_stream_t stream) {
+  if (M < 0 || K < 0 || M % 128 || K % 128) return FP8BS_ERR_SHAPE;
+  if (K / 128 > kMaxGridY || M / 128 > (int64_t)0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
+  if (M == 0 || K == 0) return FP8BS_OK;
+  if (!x || !q || !s || !qt || !st) return FP8BS_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s) || !aligned16(qt) || !aligned16(st)) return FP8BS_ERR_ALIGN;
+  if (fp8bs_status e = check_device()) return e;
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_quantize_dual(x, M, K, q, s, qt, st, flags & FP8BS_SCALE_POW2, (hipStream_t)stream));
+}
+
 fp8bs_status fp8bs_transpose_128x128(const uint8_t* q, const float* s, int64_t G, int64_t N, int64_t K, uint8_t* qt,
                                     float* st, fp8bs_stream_t stream) {
   if (G < 0 || N < 0 || N % 16 || K < 0 || K % 128) return FP8BS_ERR_SHAPE;

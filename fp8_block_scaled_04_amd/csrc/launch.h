@@ -13,6 +13,8 @@ hipError_t launch_quantize_t128x1(const uint8_t* q, const float* s, int64_t M, i
                                   bool pow2, hipStream_t stream);
 hipError_t launch_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t K, uint8_t* q, float* s, bool pow2,
                                    hipStream_t stream);
+hipError_t launch_quantize_dual(const void* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt, float* st,
+                                bool pow2, hipStream_t stream);
 hipError_t launch_transpose_128x128(const uint8_t* q, const float* s, int64_t G, int64_t N, int64_t K, uint8_t* qt,
                                    float* st, hipStream_t stream);
 hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream);

@@ -206,6 +206,112 @@ __global__ __launch_bounds__(256) void k_quantize_t128x1(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Dual quantization: the 1x128 tiles of a BF16 activation and its 128x1 tiles
+// (stored transposed) from one read of it (page 2, paragraph on hardware
+// suggestions: cast while the activations move instead of reading and
+// writing them again).  One workgroup per 128x128 tile (x = row block mb,
+// y = column block kb).
+//
+// Row pass: instruction i of wave w loads rows 32w + 4i + l/16 (sixteen
+// lanes per 256-byte row, 8 BF16 each); a row's tile amax is a DPP row max.
+// The lane writes its 8 codes (ordinary stores: the forward GEMM reads them
+// next) and stages its values in LDS.
+//
+// Column pass: lane (rg = l % 8, cg = 8w + l / 8) reads rows 16rg .. 16rg+15
+// of columns 4cg .. 4cg+3 as 8-byte LDS words, takes the column maxima over
+// them and over the 8 lanes of its column group (DPP), requantizes, and
+// writes per column 16 contiguous codes of the transposed row (8 lanes = one
+// 128-byte line).
+//
+// LDS: row r (256 bytes) holds its 8-byte word c8 at word c8 ^ 8*((r/16) % 4),
+// so the 64 lanes of a column-pass read hit 32 different words of the banks
+// (two lanes per word pair: the minimum for 64 x 8 bytes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int d_swz(int r) { return 8 * ((r >> 4) & 3); }
+__device__ __forceinline__ float bf16_at(uint2 w, int j) {
+  return j == 0 ? bf16_lo(w.x) : j == 1 ? bf16_hi(w.x) : j == 2 ? bf16_lo(w.y) : bf16_hi(w.y);
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void k_quantize_dual(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                       uint8_t* __restrict__ q, float* __restrict__ s,
+                                                       uint8_t* __restrict__ qt, float* __restrict__ st) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * 128];
+  const int64_t mb = blockIdx.x, kb = blockIdx.y;
+  const int t = threadIdx.x;
+  const int l = t & 63, w = t >> 6;
+  {
+    const int lr = l >> 4, l16 = l & 15;
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 32 * w + 4 * i + lr;
+      v[i] = nt_load16(x + (mb * 128 + r) * K + kb * 128 + l16 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 32 * w + 4 * i + lr;
+      const uint4 u = v[i];
+      float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16_lo(u.x)), __builtin_fabsf(bf16_hi(u.x))),
+                                __builtin_fmaxf(__builtin_fabsf(bf16_lo(u.y)), __builtin_fabsf(bf16_hi(u.y))));
+      float b = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16_lo(u.z)), __builtin_fabsf(bf16_hi(u.z))),
+                                __builtin_fmaxf(__builtin_fabsf(bf16_lo(u.w)), __builtin_fabsf(bf16_hi(u.w))));
+      const TileScale ts = tile_scale<POW2>(row16_max(__builtin_fmaxf(a, b)));
+      uint2 out;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(ts.sx != 1.0f) != 0, 0))
+        out = quantize8<POW2, true>(u, ts);
+      else
+        out = quantize8<POW2, false>(u, ts);
+      *reinterpret_cast<uint2*>(q + (mb * 128 + r) * K + kb * 128 + l16 * 8) = out;
+      if (l16 == 0) s[kb * M + mb * 128 + r] = ts.s;
+      *reinterpret_cast<uint4*>(tile + r * 128 + 4 * ((2 * l16) ^ d_swz(r))) = u;
+    }
+  }
+  __syncthreads();
+  const int rg = l & 7, cg = 8 * w + (l >> 3);
+  uint2 wv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 16 * rg + i;
+    wv[i] = *reinterpret_cast<const uint2*>(tile + r * 128 + 4 * (cg ^ d_swz(r)));
+  }
+  float am[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) am[j] = __builtin_fmaxf(am[j], __builtin_fabsf(bf16_at(wv[i], j)));
+  TileScale ts[4];
+  bool scaled = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ts[j] = tile_scale<POW2>(max8(am[j]));
+    scaled |= ts[j].sx != 1.0f;
+  }
+  scaled = __builtin_amdgcn_ballot_w64(scaled) != 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t packed[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float xv = bf16_at(wv[4 * k + e], j);
+        if (scaled) xv *= ts[j].sx;
+        y[e] = div_rn(xv, ts[j].ss, ts[j].r);
+      }
+      packed[k] = pack4_e4m3(y[0], y[1], y[2], y[3]);
+    }
+    nt_store16(qt + (kb * 128 + 4 * cg + j) * M + mb * 128 + 16 * rg,
+               make_uint4(packed[0], packed[1], packed[2], packed[3]));
+  }
+  if (rg == 0)
+    nt_store16(st + mb * K + kb * 128 + 4 * cg,
+               make_uint4(__builtin_bit_cast(uint32_t, ts[0].s), __builtin_bit_cast(uint32_t, ts[1].s),
+                          __builtin_bit_cast(uint32_t, ts[2].s), __builtin_bit_cast(uint32_t, ts[3].s)));
+}
+
+// ---------------------------------------------------------------------------
 // Transposed block-scaled weight (data gradient; page 2, paragraph on
 // hardware suggestions, asks for GEMMs on transposed operands).  W^T keeps
 // W's codes and takes the transposed scale grid; rows of W past N become
@@ -367,6 +473,19 @@ hipError_t launch_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t 
     hipLaunchKernelGGL(k_quantize_128x128<true>, grid, dim3(256), 0, stream, (const uint16_t*)w, N, K, q, s);
   else
     hipLaunchKernelGGL(k_quantize_128x128<false>, grid, dim3(256), 0, stream, (const uint16_t*)w, N, K, q, s);
+  return hipGetLastError();
+}
+
+// One 128x128 tile per workgroup.  Two or four tiles per workgroup with the
+// next tile's values loaded during the current one were slower on 8192x7168
+// (62 and 67 vs 45 us): twice the registers and a second barrier per tile.
+hipError_t launch_quantize_dual(const void* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt, float* st,
+                                bool pow2, hipStream_t stream) {
+  dim3 grid((unsigned)(M / 128), (unsigned)(K / 128));
+  if (pow2)
+    hipLaunchKernelGGL(k_quantize_dual<true>, grid, dim3(256), 0, stream, (const uint16_t*)x, M, K, q, s, qt, st);
+  else
+    hipLaunchKernelGGL(k_quantize_dual<false>, grid, dim3(256), 0, stream, (const uint16_t*)x, M, K, q, s, qt, st);
   return hipGetLastError();
 }
 

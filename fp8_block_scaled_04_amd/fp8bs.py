@@ -49,6 +49,7 @@ _gmask = _sig("fp8bs_grouped_gemm_fp8_masked",
               [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _U32, _P])
 _cast = _sig("fp8bs_cast_f32_to_e4m3", [_P, _I64, _P, _P])
 _t128 = _sig("fp8bs_transpose_128x128", [_P, _P, _I64, _I64, _I64, _P, _P, _P])
+_qdual = _sig("fp8bs_quantize_dual", [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P])
 _lib.fp8bs_status_str.argtypes = [ctypes.c_int]
 _lib.fp8bs_status_str.restype = ctypes.c_char_p
 _lib.fp8bs_abi_version.argtypes = []
@@ -136,6 +137,21 @@ def quantize_transpose_128x1(q: torch.Tensor, s: torch.Tensor, pow2: bool = Fals
     _check(_qt(_ptr(q), _ptr(s), M, K, _ptr(qt), _ptr(st), SCALE_POW2 if pow2 else 0, _stream(q)),
            "quantize_transpose_128x1")
     return qt, st
+
+
+def quantize_dual(x: torch.Tensor, pow2: bool = False):
+    """BF16 x[M][K] (M, K multiples of 128) -> (q, s, qt, st): 1x128 tiles
+    q[M][K], s[K/128][M] and 128x1 tiles stored transposed qt[K][M],
+    st[M/128][K], both from one read of x."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
+    s = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    qt = torch.empty((K, M), dtype=torch.float8_e4m3fn, device=x.device)
+    st = torch.empty((M // 128, K), dtype=torch.float32, device=x.device)
+    _check(_qdual(_ptr(x), M, K, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), SCALE_POW2 if pow2 else 0, _stream(x)),
+           "quantize_dual")
+    return q, s, qt, st
 
 
 def quantize_128x128(w: torch.Tensor, pow2: bool = False):

@@ -127,6 +127,25 @@ fp8bs_status fp8bs_quantize_transpose_128x1(const uint8_t* q, const float* s,
                                             fp8bs_stream_t stream);
 
 /*
+ * Dual quantization of a BF16 activation from one read of it (page 2, "A
+ * Deadly Mistake Uncovered on Deepseek China Ai", paragraph on hardware
+ * suggestions: quantize while activations move instead of reading and
+ * writing them again).  Produces the 1x128 tiles of x (the forward GEMM's A
+ * operand) and the 128x1 tiles of x stored transposed (the weight
+ * gradient's operand), both quantized from the BF16 values: qt/st equal the
+ * 1x128 quantization of x^T.  (fp8bs_quantize_transpose_128x1 instead
+ * requantizes the cached FP8 copy, as page 1 describes.)
+ *   x  : BF16 [M][K]                              (input)
+ *   q  : E4M3 [M][K],  s  : FP32 [K/128][M]       (1x128 tiles)
+ *   qt : E4M3 [K][M],  st : FP32 [M/128][K]       (128x1 tiles, transposed)
+ * Requires M >= 0, K >= 0, M % 128 == 0, K % 128 == 0.  flags: 0 or
+ * FP8BS_SCALE_POW2.
+ */
+fp8bs_status fp8bs_quantize_dual(const void* x, int64_t M, int64_t K,
+                                 uint8_t* q, float* s, uint8_t* qt, float* st,
+                                 uint32_t flags, fp8bs_stream_t stream);
+
+/*
  * 128x128 block quantization of (optionally batched) weights: one scale per
  * block of up to 128 rows x 128 columns; a partial last row block uses its
  * valid rows only.  Weights for the GEMMs below are laid out this way.

@@ -46,7 +46,7 @@ def lib(lib_path):
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in fp8bs.h but not exported"
 
@@ -188,3 +188,15 @@ def test_transpose_weight_validation(lib):
     assert f(MIS, FAKE, 1, 128, 256, FAKE, FAKE, None) == ALIGN
     if NO_DEVICE:
         assert f(FAKE, FAKE, 1, 144, 256, FAKE, FAKE, None) == DEVICE
+
+
+def test_quantize_dual_validation(lib):
+    f = fn(lib, "fp8bs_quantize_dual", [P, I64, I64, P, P, P, P, U32, P])
+    assert f(FAKE, 100, 128, FAKE, FAKE, FAKE, FAKE, 0, None) == SHAPE      # M % 128
+    assert f(FAKE, 128, 200, FAKE, FAKE, FAKE, FAKE, 0, None) == SHAPE      # K % 128
+    assert f(FAKE, 128, 128, FAKE, FAKE, FAKE, FAKE, 2, None) == FLAGS
+    assert f(None, 0, 128, None, None, None, None, 0, None) == OK          # empty
+    assert f(FAKE, 128, 128, FAKE, FAKE, None, FAKE, 1, None) == NULL
+    assert f(FAKE, 128, 128, FAKE, FAKE, FAKE, MIS, 0, None) == ALIGN
+    if NO_DEVICE:
+        assert f(FAKE, 128, 128, FAKE, FAKE, FAKE, FAKE, 0, None) == DEVICE

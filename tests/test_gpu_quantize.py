@@ -148,3 +148,39 @@ def test_cast_f32_to_e4m3():
     q = fp8bs.cast_to_e4m3(f32_dev(x))
     torch.cuda.synchronize()
     assert_codes_equal(codes_host(q), e4m3.encode(x), "cast")
+
+
+def check_dual(bits, pow2, what):
+    q, s, qt, st = fp8bs.quantize_dual(bf16_dev(bits), pow2)
+    torch.cuda.synchronize()
+    rq, rs, rqt, rst = quantize.quantize_dual(bits, pow2)
+    assert_codes_equal(codes_host(q), rq, what + " 1x128 codes")
+    assert_codes_equal(f32_bits_host(s), rs.view(np.uint32), what + " 1x128 scales")
+    assert_codes_equal(codes_host(qt), rqt, what + " 128x1 codes")
+    assert_codes_equal(f32_bits_host(st), rst.view(np.uint32), what + " 128x1 scales")
+
+
+@pytest.mark.parametrize("M,K", [(128, 128), (256, 384), (384, 256), (128, 1536), (1024, 640)])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_quantize_dual_workload_recipe(M, K, pow2):
+    print(f"quantize_dual M={M} K={K} pow2={pow2}", flush=True)
+    check_dual(synth.activation(M, K, seed=M + 3 * K)["a"], pow2, f"dual {M}x{K}")
+
+
+def test_quantize_dual_special_tiles():
+    # zero tiles, a constant tile, tiny values (the 2^64 pre-scaling path),
+    # negative zeros, and one huge value per column tile
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((256, 256)) * 0.5).astype(np.float32)
+    x[:128, :128] = 0.0
+    x[128:, :128] = 3.0
+    x[:128, 128:] *= 2.0 ** -100
+    x[5, 200] = -0.0
+    x[128 + 17, 128 + 3] = 3.0e38
+    check_dual(synth.bf16_bits(x), False, "dual special")
+    check_dual(synth.bf16_bits(x), True, "dual special pow2")
+
+
+def test_quantize_dual_full_size():
+    print("quantize_dual full size 8192x7168", flush=True)
+    check_dual(synth.activation(8192, 7168, seed=1)["a"], False, "dual 8192x7168")
