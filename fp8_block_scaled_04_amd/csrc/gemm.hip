@@ -46,24 +46,23 @@ namespace {
 
 constexpr int kKC = 128;  // K chunk = promotion interval = MFMA K
 
-template <int BM_, int BN_, int WGM_, int WGN_, bool DB_, int S_ = 2, int PF_ = 0, bool CS_ = false>
+template <int BM_, int BN_, int WGM_, int WGN_, bool DB_, int S_ = 2, bool CS_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
   static constexpr bool DB = DB_;                   // fragments double buffered in registers
   static constexpr int S = S_;                      // LDS stages (chunks in flight + 1)
-  static constexpr int PF = PF_;                    // weight chunks prefetched into L2 beyond the stages
   static constexpr int NW = WGM * WGN;              // waves per workgroup
   static constexpr int THREADS = 64 * NW;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int FM = WM / 16, FN = WN / 16;  // 16x16 fragments per wave
   static constexpr int A_BYTES = BM * kKC;
   static constexpr int B_BYTES = BN * kKC;
-  // One scale DMA per wave and chunk (64 floats): slots 0..BM/64-1 hold the
-  // activation scales of the tile's rows, slot BM/64 the weight scales of
-  // weight block rows n0/128 + i; any further slots hold copies of it.  With
-  // compact scales (CS) the further waves write their identical copy into
-  // slot BM/64 itself, which frees LDS for a third stage (not for the weight
-  // gradient, whose per-row weight scales need every slot).
+  // Scale DMAs (64 floats each): waves 0..BM/64-1 fetch the activation
+  // scales of the tile's rows into slots 0..BM/64-1, wave BM/64 the weight
+  // scales of weight block rows n0/128 + i into slot BM/64 (the weight
+  // gradient: waves BM/64.. the per-row weight scales, one slot per 64 rows).
+  // Compact scales (CS) keep only the slots the dense and grouped modes use,
+  // which frees LDS for a third stage of the 256x160 tile.
   static constexpr int SA_WAVES = BM / 64;
   static constexpr bool CS = CS_;
   static constexpr int SC_BYTES = CS ? (SA_WAVES + 1) * 256 : NW * 256;
@@ -71,19 +70,18 @@ struct Cfg {
   static constexpr int SB_OFF = A_BYTES + B_BYTES + SA_WAVES * 256;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   static constexpr int A_LOADS = BM / (8 * NW);     // 8 rows of 128 bytes per wave instruction
-  static constexpr int B_LOADS = BN / (8 * NW);     // whole 16-byte instructions
-  // Weight rows that do not split evenly over the waves (BN % (8 NW)) are
-  // loaded 4 bytes per lane: 2 rows per wave, 16 rows per instruction.
-  static constexpr int B_TAIL_ROWS = BN % (8 * NW);
-  static constexpr int B_TAIL_LOADS = B_TAIL_ROWS / (2 * NW);
-  static constexpr int JUNK_OFF = S * STAGE;
-  static constexpr int LDS_BYTES = S * STAGE + (PF > 0 ? 1024 : 0);
-  // L2 prefetch of a weight chunk: one dword per 64-byte half row, 32 rows
-  // per instruction, landing in the scratch kilobyte.
-  static constexpr int PF_LOADS = PF > 0 ? (BN + 32 * NW - 1) / (32 * NW) : 0;
+  // Weight rows go in groups of 8 (one 16-byte-per-lane instruction each),
+  // dealt round-robin: every wave issues B_FULL, waves below B_EXTRA one
+  // more and the others repeat one of theirs.  (Every DMA instruction costs
+  // the texture unit about the same time whatever its width: the 4-byte
+  // loads that had carried the last 32 rows of 160 cost 7 % on 4096x2112.)
+  static constexpr int B_GROUPS = BN / 8;
+  static constexpr int B_FULL = B_GROUPS / NW;
+  static constexpr int B_EXTRA = B_GROUPS % NW;
+  static_assert(B_EXTRA == 0 || B_FULL >= 1, "a wave without an extra group repeats one of its own");
+  static constexpr int LDS_BYTES = S * STAGE;
   static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES;
   static_assert(BM % (8 * NW) == 0 && BN % 16 == 0, "A rows split evenly over the waves; B rows are fragments");
-  static_assert(B_TAIL_ROWS % (2 * NW) == 0, "the weight tail splits into 2-row pieces per wave");
   static_assert(SA_WAVES < NW, "one wave must be left for the weight scales");
   static_assert(WN % 16 == 0 && WN <= 128, "a wave's columns are whole fragments within at most two weight blocks");
   static_assert(DB_ == false || 128 % WN == 0, "the double-buffered path needs a wave's columns in one weight block");
@@ -96,7 +94,7 @@ using LargeTile = Cfg<256, 256, 4, 2, false>;
 // 256x160 with three stages (compact scales: 160 KB of LDS): measured on
 // 4096x2112x7168 right after the quantizer wrote A, 87 -> 78 us, and 96 ->
 // 83 us with cold caches; two stages for the weight gradient.
-using MidTile = Cfg<256, 160, 4, 2, false, 3, 0, true>;
+using MidTile = Cfg<256, 160, 4, 2, false, 3, true>;
 using WgradMidTile = Cfg<256, 160, 4, 2, false>;
 // Memory-bound shapes (few rows): 128x96 tiles, three stages, one
 // workgroup per CU on the 24576-column decode projection.
@@ -363,18 +361,26 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   const uint32_t row_off = (uint32_t)(((wave * 8 + (lane >> 3)) * K) +
                                       (((lane & 7) ^ (((wave & 1) << 2) + (lane >> 4))) * 16));
   const uint32_t row_step = (uint32_t)(C::NW * 8 * K);
-  // Scale DMA of this wave (one dword per lane per chunk, no branches):
-  // waves below SA_WAVES fetch activation scales of rows m0 + 64*wave + lane,
-  // the others the weight scale of block row n0/128 + lane (both clamped).
-  // (kWgrad: the other waves fetch weight-row scales n0 + 64*(wave -
+  // Scale DMA of this wave (one dword per lane per chunk): waves below
+  // SA_WAVES fetch activation scales of rows m0 + 64*wave + lane, wave
+  // SA_WAVES the weight scale of block row n0/128 + lane (both clamped).
+  // (kWgrad: waves SA_WAVES .. SCW-1 fetch weight-row scales n0 + 64*(wave -
   // SA_WAVES) + lane from the [K/128][N] layout, landing right after the
-  // activation scales.)
-  const bool sa_wave = wave < C::SA_WAVES;
-  int64_t sa_row = m0 + (sa_wave ? wave : 0) * 64 + lane;
+  // activation scales.)  Waves from SCW on repeat wave SCW-1's DMA (the same
+  // bytes to the same LDS slot): every wave then issues the same number of
+  // DMAs per chunk, so the waits are compile-time constants and the loop has
+  // no per-wave branches (which split its scheduling regions and made the
+  // register allocator spill).
+  constexpr int SCW = C::SA_WAVES + (MODE == kWgrad ? (BN + 63) / 64 : 1);
+  static_assert(SCW <= C::NW, "every scale slot needs a wave");
+  static_assert(!C::CS || SCW <= C::SA_WAVES + 1, "compact scales hold one weight-scale slot");
+  const int scw = wave < SCW ? wave : SCW - 1;   // the scale DMA this wave issues
+  const bool sa_wave = scw < C::SA_WAVES;
+  int64_t sa_row = m0 + (sa_wave ? scw : 0) * 64 + lane;
   if (sa_row > m_alloc - 1) sa_row = m_alloc - 1;
   int64_t sb_blk = n0 / 128 + lane;
   if (sb_blk > NB - 1) sb_blk = NB - 1;
-  int64_t sb_row = n0 + (sa_wave ? 0 : wave - C::SA_WAVES) * 64 + lane;
+  int64_t sb_row = n0 + (sa_wave ? 0 : scw - C::SA_WAVES) * 64 + lane;
   if (sb_row > N - 1) sb_row = N - 1;
   const v4i rsb_w = make_rsrc(sb_base, (int64_t)KT * N * 4);
   const v4i rsc = sa_wave ? rsa : (MODE == kWgrad ? rsb_w : rsb);
@@ -404,35 +410,17 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     for (int i = 0; i < C::A_LOADS; ++i)
       dma16(rak, st + (i * C::NW + wave) * 8 * kKC, ro + i * row_step, koff);
 #pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i)
+    for (int i = 0; i < C::B_FULL; ++i)
       dma16(rbk, st + C::A_BYTES + (i * C::NW + wave) * 8 * kKC, ro + i * row_step, koff);
-    // Tail rows: instruction i, wave w covers rows t0 = B_LOADS*8*NW + 16i + 2w
-    // and t0+1; lane l writes LDS word l (row t0 + l/32, physical word l%32 of
-    // the swizzled row) from the logical segment that belongs there.
-#pragma unroll
-    for (int i = 0; i < C::B_TAIL_LOADS; ++i) {
-      const int t0 = C::B_LOADS * 8 * C::NW + 16 * i + 2 * wave;
-      const int row = t0 + (lane >> 5), pw = lane & 31;
-      const uint32_t voff = (uint32_t)(row * K + 16 * ((pw >> 2) ^ swz(row)) + 4 * (pw & 3));
-      dma4(rbk, st + C::A_BYTES + t0 * kKC, voff, koff);
+    // Weight group B_FULL*NW + wave for waves below B_EXTRA; the others
+    // repeat their last group (same bytes, same LDS rows).
+    if constexpr (C::B_EXTRA > 0) {
+      const int bi = wave < C::B_EXTRA ? C::B_FULL : C::B_FULL - 1;
+      dma16(rbk, st + C::A_BYTES + (bi * C::NW + wave) * 8 * kKC, ro + bi * row_step, koff);
     }
-    dma4(rck, st + C::SA_OFF + ((C::CS && wave > C::SA_WAVES) ? C::SA_WAVES : wave) * 256, sc_voff, soff);
+    dma4(rck, st + C::SA_OFF + scw * 256, sc_voff, soff);
   };
-  // Weight chunk kb into L2 (nothing is read back): lane l of instruction i
-  // touches row 32*(i*NW + wave) + l/2, half row l%2.  Rows past the tile
-  // fail the range check of the descriptor and fetch nothing.
-  auto prefetch = [&](int kb) {
-    if constexpr (C::PF > 0) {
-      const bool live = kb < KT;
-      const uint32_t koff = live ? (uint32_t)kb * kKC : 0u;
-      const v4i rbk = live ? rb : r_none;
-#pragma unroll
-      for (int i = 0; i < C::PF_LOADS; ++i)
-        dma4(rbk, smem_lds + C::JUNK_OFF, (uint32_t)((32 * (i * C::NW + wave) + (lane >> 1)) * K + (lane & 1) * 64),
-             koff);
-    }
-  };
-  constexpr int DMA_PER_CHUNK = C::A_LOADS + C::B_LOADS + C::B_TAIL_LOADS + 1 + C::PF_LOADS;   // vmcnt of one issue() + prefetch()
+  constexpr int DPC = C::A_LOADS + C::B_FULL + (C::B_EXTRA > 0 ? 1 : 0) + 1;   // DMA instructions per issue()
   // ---- per-lane fragment read offsets -----------------------------------
   const int fr = lane & 15, fg = lane >> 4;
   const uint32_t rd0 = fr * kKC + 16 * (fg ^ swz(fr));
@@ -783,12 +771,9 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     // 0 has landed in every wave's share, its first fragments are read.
     constexpr int S = C::S;
 #pragma unroll
-    for (int c = 0; c < S; ++c) {
-      issue(c, c);
-      prefetch(S + c);
-    }
-    // chunks 1 .. S-1 (and their prefetches) may still be in flight
-    wait_vm_lgkm0<(S - 1) * DMA_PER_CHUNK + C::PF_LOADS>();
+    for (int c = 0; c < S; ++c) issue(c, c);
+    // chunks 1 .. S-1 may still be in flight
+    wait_vm_lgkm0<(S - 1) * DPC>();
     __builtin_amdgcn_s_barrier();
     read_a1(0, 0);
     read_b1(0, 0);
@@ -812,13 +797,10 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       last_row(stage + 1 == S ? 0 : stage + 1, scp,
                [&] {
-                 wait_vm_lgkm0<(S - 2) * DMA_PER_CHUNK + C::PF_LOADS>();
+                 wait_vm_lgkm0<(S - 2) * DPC>();
                  __builtin_amdgcn_s_barrier();
                },
-               [&] {
-                 issue(kb + S, stage);
-                 prefetch(kb + 2 * S);
-               });
+               [&] { issue(kb + S, stage); });
     };
     int kb = 0;
     for (; kb + S - 1 < KT; kb += S) {
