@@ -21,14 +21,17 @@ constexpr float kE4M3Max = 448.0f;
 // half-mirror and mirror steps then join the quads of an 8-lane half and the
 // two halves of the row, so every lane ends with the row's maximum.
 // ---------------------------------------------------------------------------
+// Every lane reads a lane of its own row, so no lane is out of range and the
+// DPP move carries no "old" value; that lets the compiler fold it into the
+// max as a DPP operand (one instruction per step).
 __device__ __forceinline__ float dpp_max_step(float v, int ctrl_id) {
   int iv = __builtin_bit_cast(int, v);
   int o;
   switch (ctrl_id) {
-    case 0: o = __builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false); break;  // quad_perm 1,0,3,2
-    case 1: o = __builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false); break;  // quad_perm 2,3,0,1
-    case 2: o = __builtin_amdgcn_update_dpp(iv, iv, 0x141, 0xF, 0xF, false); break; // row_half_mirror
-    default: o = __builtin_amdgcn_update_dpp(iv, iv, 0x140, 0xF, 0xF, false); break; // row_mirror
+    case 0: o = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true); break;  // quad_perm 1,0,3,2
+    case 1: o = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true); break;  // quad_perm 2,3,0,1
+    case 2: o = __builtin_amdgcn_mov_dpp(iv, 0x141, 0xF, 0xF, true); break; // row_half_mirror
+    default: o = __builtin_amdgcn_mov_dpp(iv, 0x140, 0xF, 0xF, true); break; // row_mirror
   }
   return __builtin_fmaxf(v, __builtin_bit_cast(float, o));
 }

@@ -13,6 +13,8 @@
 //
 // All four kernels are bound by HBM bandwidth: 128-bit loads and stores, tile
 // amax by DPP row reductions, no LDS except for the transpose.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -37,6 +39,90 @@ __device__ __forceinline__ void nt_store16(void* p, uint4 v) {
 }
 
 // ---------------------------------------------------------------------------
+// Batched tile scales.  A lane holds partial maxima of several tiles, each
+// tile spread over a group of lanes.  A reduce-scatter across the group (at
+// each exchange a lane keeps half of its tiles and takes the maximum with its
+// partner's copy of that half, the partner keeping the other half) leaves
+// every lane with the full maximum of one tile, so a lane computes a single
+// tile scale and DPP broadcasts give every lane the scales of the tiles it
+// quantizes.  Every DPP source lane lies inside its row (no lane is out of
+// range).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm 1,0,3,2: lane i ^ 1
+constexpr int kDppXor2 = 0x4E;         // quad_perm 2,3,0,1: lane i ^ 2
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i ^ 7 (within 8 lanes)
+constexpr int kDppXor8 = 0x128;        // row_ror:8: lane i ^ 8 (within the row of 16)
+constexpr int kDppRowBcast = 0x150;    // row_newbcast:n: lane n of the row
+
+// Lane j of the quad, to every lane of the quad.
+__device__ __forceinline__ float quad_bcast(float v, int j) {
+  switch (j) {
+    case 0: return dpp<0x00>(v);
+    case 1: return dpp<0x55>(v);
+    case 2: return dpp<0xAA>(v);
+    default: return dpp<0xFF>(v);
+  }
+}
+// Lane n (even) of the row, to every lane of the row.
+__device__ __forceinline__ float row_bcast(float v, int n) {
+  switch (n) {
+    case 0: return dpp<kDppRowBcast + 0>(v);
+    case 2: return dpp<kDppRowBcast + 2>(v);
+    case 4: return dpp<kDppRowBcast + 4>(v);
+    case 6: return dpp<kDppRowBcast + 6>(v);
+    case 8: return dpp<kDppRowBcast + 8>(v);
+    case 10: return dpp<kDppRowBcast + 10>(v);
+    case 12: return dpp<kDppRowBcast + 12>(v);
+    default: return dpp<kDppRowBcast + 14>(v);
+  }
+}
+// One exchange: of its 2H values the lane keeps the upper half if `upper`,
+// else the lower, and sends the other half to its partner (lane CTRL names).
+template <int CTRL, int H>
+__device__ __forceinline__ void scatter_max(const float (&v)[2 * H], float (&out)[H], bool upper) {
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const float keep = upper ? v[H + k] : v[k];
+    const float send = upper ? v[k] : v[H + k];
+    out[k] = __builtin_fmaxf(keep, dpp<CTRL>(send));
+  }
+}
+// am: the lane's maxima of four columns whose lanes are the 8 of its half
+// row.  Returns the maximum of column (lane & 3) over those 8 lanes.
+__device__ __forceinline__ float colgroup_max(const float (&am)[4], int lane) {
+  float a[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = __builtin_fmaxf(am[j], dpp<kDppHalfMirror>(am[j]));
+  float b[2], c[1];
+  scatter_max<kDppXor2, 2>(a, b, (lane & 2) != 0);
+  scatter_max<kDppXor1, 1>(b, c, (lane & 1) != 0);
+  return c[0];
+}
+// am: the lane's maxima of eight tiles spread over its row of 16 lanes.
+// Returns the row maximum of tile (lane >> 1) & 7.
+__device__ __forceinline__ float row_max8(const float (&am)[8], int lane) {
+  float a[4], b[2], c[1];
+  scatter_max<kDppXor8, 4>(am, a, (lane & 8) != 0);
+  scatter_max<kDppHalfMirror, 2>(a, b, (lane & 4) != 0);   // partner i ^ 7: the other bit-2 half
+  scatter_max<kDppXor2, 1>(b, c, (lane & 2) != 0);
+  return __builtin_fmaxf(c[0], dpp<kDppXor1>(c[0]));
+}
+// am: the lane's maxima of two tiles spread over its row of 16 lanes.
+// Returns the row maximum of tile (lane >> 3) & 1.
+__device__ __forceinline__ float row_max2(const float (&am)[2], int lane) {
+  float a[1];
+  scatter_max<kDppXor8, 1>(am, a, (lane & 8) != 0);
+  float v = a[0];
+  v = __builtin_fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = __builtin_fmaxf(v, dpp<kDppXor2>(v));
+  return __builtin_fmaxf(v, dpp<kDppXor1>(v));
+}
+
+// ---------------------------------------------------------------------------
 // 1x128: one tile = 16 lanes (one DPP row) x 8 BF16 each (one 16-byte load).
 // A workgroup of 256 lanes covers 16 rows; each lane walks kQ1Tiles tiles of its
 // row so that kQ1Tiles loads are in flight before any arithmetic.  Scales of 16
@@ -52,6 +138,15 @@ __device__ __forceinline__ uint2 quantize8(uint4 v, const TileScale& t) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = div_rn(SCALED ? x[i] * t.sx : x[i], t.ss, t.r);
   return make_uint2(pack4_e4m3(y[0], y[1], y[2], y[3]), pack4_e4m3(y[4], y[5], y[6], y[7]));
+}
+
+// max |x| over the 8 BF16 of a 16-byte word
+__device__ __forceinline__ float absmax8(uint4 w) {
+  const float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16_lo(w.x)), __builtin_fabsf(bf16_hi(w.x))),
+                                  __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.y)), __builtin_fabsf(bf16_hi(w.y))));
+  const float b = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16_lo(w.z)), __builtin_fabsf(bf16_hi(w.z))),
+                                  __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.w)), __builtin_fabsf(bf16_hi(w.w))));
+  return __builtin_fmaxf(a, b);
 }
 
 template <bool POW2>
@@ -71,26 +166,76 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(const uint16_t* __restri
     if (row_ok && kb < KT)
       v[t] = nt_load16(x + m * K + kb * 128 + lane16 * 8);
   }
+  static_assert(kQ1Tiles == 2, "the tile maxima are reduced two at a time");
+  float am[kQ1Tiles];
 #pragma unroll
-  for (int t = 0; t < kQ1Tiles; ++t) {
-    const int64_t kb = kb0 + t;
-    const uint4 w = v[t];
-    float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16_lo(w.x)), __builtin_fabsf(bf16_hi(w.x))),
-                              __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.y)), __builtin_fabsf(bf16_hi(w.y))));
-    float b = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16_lo(w.z)), __builtin_fabsf(bf16_hi(w.z))),
-                              __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.w)), __builtin_fabsf(bf16_hi(w.w))));
-    const float amax = row16_max(__builtin_fmaxf(a, b));
-    const TileScale ts = tile_scale<POW2>(amax);
-    uint2 out;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(ts.sx != 1.0f) != 0, 0))
-      out = quantize8<POW2, true>(w, ts);
-    else
-      out = quantize8<POW2, false>(w, ts);
-    if (row_ok && kb < KT) {
-      *reinterpret_cast<uint2*>(q + m * K + kb * 128 + lane16 * 8) = out;
-      if (lane16 == 0) s[kb * M + m] = ts.s;
+  for (int t = 0; t < kQ1Tiles; ++t) am[t] = absmax8(v[t]);
+  // Lane l16 computes the scale of tile (l16 >> 3); tile t's is broadcast
+  // from lane 8t of the row.
+  const TileScale mine = tile_scale<POW2>(row_max2(am, lane16));
+  auto run = [&](auto scaled) {
+    constexpr bool SC = decltype(scaled)::value;
+#pragma unroll
+    for (int t = 0; t < kQ1Tiles; ++t) {
+      const int64_t kb = kb0 + t;
+      TileScale ts;
+      ts.ss = row_bcast(mine.ss, 8 * t);
+      ts.r = row_bcast(mine.r, 8 * t);
+      ts.sx = SC ? row_bcast(mine.sx, 8 * t) : 1.0f;
+      const uint2 out = quantize8<POW2, SC>(v[t], ts);
+      if (row_ok && kb < KT) *reinterpret_cast<uint2*>(q + m * K + kb * 128 + lane16 * 8) = out;
     }
+  };
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(mine.sx != 1.0f) != 0, 0))
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+  const int64_t kbs = kb0 + (lane16 >> 3);
+  if (row_ok && (lane16 & 7) == 0 && kbs < KT) s[kbs * M + m] = mine.s;
+}
+
+// Sixteen values of one tile -> sixteen codes (byte i = value i).  SCALED:
+// the tile is one of those with amax < 2^-60, evaluated on x * 2^64.  The
+// callers branch on a wave-uniform flag, so the common case carries no
+// per-element multiply or select.
+template <bool SCALED>
+__device__ __forceinline__ uint4 quantize16(const float (&x)[16], const TileScale& t) {
+  uint32_t packed[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = div_rn(SCALED ? x[4 * k + e] * t.sx : x[4 * k + e], t.ss, t.r);
+    packed[k] = pack4_e4m3(y[0], y[1], y[2], y[3]);
   }
+  return make_uint4(packed[0], packed[1], packed[2], packed[3]);
+}
+
+// The column pass shared by the transposing quantizers.  The lane holds 16
+// rows of four columns (d[j][i]: column j, row i; am[j]: their maxima); the
+// 8 lanes of its half row hold the column group's 128 rows.  Lane l computes
+// the scale of column l & 3 and writes it (lanes 0..3 of the group, to
+// srow[l & 3]); column j's codes go to qrow + j * ld as 16 contiguous bytes.
+template <bool POW2>
+__device__ __forceinline__ void requant_columns(const float (&d)[4][16], const float (&am)[4], int l,
+                                                uint8_t* qrow, int64_t ld, float* srow) {
+  const TileScale mine = tile_scale<POW2>(colgroup_max(am, l));
+  auto run = [&](auto scaled) {
+    constexpr bool SC = decltype(scaled)::value;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      TileScale ts;
+      ts.ss = quad_bcast(mine.ss, j);
+      ts.r = quad_bcast(mine.r, j);
+      ts.sx = SC ? quad_bcast(mine.sx, j) : 1.0f;
+      nt_store16(qrow + j * ld, quantize16<SC>(d[j], ts));
+    }
+  };
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(mine.sx != 1.0f) != 0, 0))
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+  if ((l & 4) == 0) __builtin_nontemporal_store(mine.s, srow + (l & 3));
 }
 
 // ---------------------------------------------------------------------------
@@ -114,14 +259,6 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int t_row(int r) { return r + (r >= 64 ? 1 : 0); }
 __device__ __forceinline__ int t_swz(int r) { return 8 * ((r >> 4) & 3); }
-
-// Maximum over the 8 adjacent lanes l & ~7 .. l | 7 (DPP within a row of 16).
-__device__ __forceinline__ float max8(float v) {
-  v = dpp_max_step(v, 0);   // lanes xor 1
-  v = dpp_max_step(v, 1);   // lanes xor 2
-  v = dpp_max_step(v, 2);   // mirror within each half row of 8
-  return v;
-}
 
 template <bool POW2>
 __global__ __launch_bounds__(256) void k_quantize_t128x1(const uint8_t* __restrict__ q, const float* __restrict__ s,
@@ -165,44 +302,17 @@ __global__ __launch_bounds__(256) void k_quantize_t128x1(const uint8_t* __restri
     const float4 f = *reinterpret_cast<const float4*>(rs + 16 * rg + 4 * i);
     rsv[4 * i] = f.x; rsv[4 * i + 1] = f.y; rsv[4 * i + 2] = f.z; rsv[4 * i + 3] = f.w;
   }
-  float d[16][4];
+  float d[4][16];
   float am[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 16; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      d[i][j] = e4m3_to_f32(wv[i], j) * rsv[i];
-      am[j] = __builtin_fmaxf(am[j], __builtin_fabsf(d[i][j]));
+      d[j][i] = e4m3_to_f32(wv[i], j) * rsv[i];
+      am[j] = __builtin_fmaxf(am[j], __builtin_fabsf(d[j][i]));
     }
-  TileScale ts[4];
-  bool scaled = false;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ts[j] = tile_scale<POW2>(max8(am[j]));
-    scaled |= ts[j].sx != 1.0f;
-  }
-  scaled = __builtin_amdgcn_ballot_w64(scaled) != 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t packed[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float y[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float xv = d[4 * k + e][j];
-        if (scaled) xv *= ts[j].sx;
-        y[e] = div_rn(xv, ts[j].ss, ts[j].r);
-      }
-      packed[k] = pack4_e4m3(y[0], y[1], y[2], y[3]);
-    }
-    nt_store16(qt + (kb * 128 + 4 * c4 + j) * M + mb * 128 + 16 * rg,
-               make_uint4(packed[0], packed[1], packed[2], packed[3]));
-  }
-  if (rg == 0)
-    nt_store16(st + mb * K + kb * 128 + 4 * c4,
-               make_uint4(__builtin_bit_cast(uint32_t, ts[0].s), __builtin_bit_cast(uint32_t, ts[1].s),
-                          __builtin_bit_cast(uint32_t, ts[2].s), __builtin_bit_cast(uint32_t, ts[3].s)));
+  requant_columns<POW2>(d, am, l, qt + (kb * 128 + 4 * c4) * M + mb * 128 + 16 * rg, M,
+                        st + mb * K + kb * 128 + 4 * c4);
 }
 
 // ---------------------------------------------------------------------------
@@ -248,24 +358,33 @@ __global__ __launch_bounds__(256) void k_quantize_dual(const uint16_t* __restric
       const int r = 32 * w + 4 * i + lr;
       v[i] = nt_load16(x + (mb * 128 + r) * K + kb * 128 + l16 * 8);
     }
+    float am[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 32 * w + 4 * i + lr;
-      const uint4 u = v[i];
-      float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16_lo(u.x)), __builtin_fabsf(bf16_hi(u.x))),
-                                __builtin_fmaxf(__builtin_fabsf(bf16_lo(u.y)), __builtin_fabsf(bf16_hi(u.y))));
-      float b = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16_lo(u.z)), __builtin_fabsf(bf16_hi(u.z))),
-                                __builtin_fmaxf(__builtin_fabsf(bf16_lo(u.w)), __builtin_fabsf(bf16_hi(u.w))));
-      const TileScale ts = tile_scale<POW2>(row16_max(__builtin_fmaxf(a, b)));
-      uint2 out;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(ts.sx != 1.0f) != 0, 0))
-        out = quantize8<POW2, true>(u, ts);
-      else
-        out = quantize8<POW2, false>(u, ts);
-      *reinterpret_cast<uint2*>(q + (mb * 128 + r) * K + kb * 128 + l16 * 8) = out;
-      if (l16 == 0) s[kb * M + mb * 128 + r] = ts.s;
-      *reinterpret_cast<uint4*>(tile + r * 128 + 4 * ((2 * l16) ^ d_swz(r))) = u;
+      am[i] = absmax8(v[i]);
+      *reinterpret_cast<uint4*>(tile + r * 128 + 4 * ((2 * l16) ^ d_swz(r))) = v[i];
     }
+    // Lane l16 computes the scale of tile (row) (l16 >> 1) & 7 of the eight
+    // its row of lanes covers; tile i's is broadcast from lane 2i.
+    const TileScale mine = tile_scale<POW2>(row_max8(am, l16));
+    auto run = [&](auto scaled) {
+      constexpr bool SC = decltype(scaled)::value;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 32 * w + 4 * i + lr;
+        TileScale ts;
+        ts.ss = row_bcast(mine.ss, 2 * i);
+        ts.r = row_bcast(mine.r, 2 * i);
+        ts.sx = SC ? row_bcast(mine.sx, 2 * i) : 1.0f;
+        *reinterpret_cast<uint2*>(q + (mb * 128 + r) * K + kb * 128 + l16 * 8) = quantize8<POW2, SC>(v[i], ts);
+      }
+    };
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mine.sx != 1.0f) != 0, 0))
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+    if ((l16 & 1) == 0) s[kb * M + mb * 128 + 32 * w + 4 * (l16 >> 1) + lr] = mine.s;
   }
   __syncthreads();
   const int rg = l & 7, cg = 8 * w + (l >> 3);
@@ -275,40 +394,17 @@ __global__ __launch_bounds__(256) void k_quantize_dual(const uint16_t* __restric
     const int r = 16 * rg + i;
     wv[i] = *reinterpret_cast<const uint2*>(tile + r * 128 + 4 * (cg ^ d_swz(r)));
   }
+  float d[4][16];
   float am[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 16; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) am[j] = __builtin_fmaxf(am[j], __builtin_fabsf(bf16_at(wv[i], j)));
-  TileScale ts[4];
-  bool scaled = false;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ts[j] = tile_scale<POW2>(max8(am[j]));
-    scaled |= ts[j].sx != 1.0f;
-  }
-  scaled = __builtin_amdgcn_ballot_w64(scaled) != 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t packed[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float y[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float xv = bf16_at(wv[4 * k + e], j);
-        if (scaled) xv *= ts[j].sx;
-        y[e] = div_rn(xv, ts[j].ss, ts[j].r);
-      }
-      packed[k] = pack4_e4m3(y[0], y[1], y[2], y[3]);
+    for (int j = 0; j < 4; ++j) {
+      d[j][i] = bf16_at(wv[i], j);
+      am[j] = __builtin_fmaxf(am[j], __builtin_fabsf(d[j][i]));
     }
-    nt_store16(qt + (kb * 128 + 4 * cg + j) * M + mb * 128 + 16 * rg,
-               make_uint4(packed[0], packed[1], packed[2], packed[3]));
-  }
-  if (rg == 0)
-    nt_store16(st + mb * K + kb * 128 + 4 * cg,
-               make_uint4(__builtin_bit_cast(uint32_t, ts[0].s), __builtin_bit_cast(uint32_t, ts[1].s),
-                          __builtin_bit_cast(uint32_t, ts[2].s), __builtin_bit_cast(uint32_t, ts[3].s)));
+  requant_columns<POW2>(d, am, l, qt + (kb * 128 + 4 * cg) * M + mb * 128 + 16 * rg, M,
+                        st + mb * K + kb * 128 + 4 * cg);
 }
 
 // ---------------------------------------------------------------------------
