@@ -230,6 +230,50 @@ def extra_kernels(fb, synth):
     return out
 
 
+def vs_hipblaslt(fb, synth, reps=5, burst=20):
+    """Context, not part of the step: the block-scaled GEMM beside hipBLASLt's
+    plain FP8 GEMM (torch._scaled_mm with one scale per tensor, and with one
+    per row of A and column of B) on the same FP8 operand bytes (the
+    quantized synthetic workload).  The library applies no 1x128 / 128x128
+    block scales, so per output it does strictly less work.  Interleaved
+    bursts of `burst` back-to-back calls between two events; medians in us."""
+    out = {}
+    for (M, N, K) in [(4096, 2112, 7168), (8192, 4096, 7168)]:
+        w = synth.dense(M, N, K, seed=1)
+        a, sa = fb.quantize_1x128(dev_bf16(w["a"]))
+        b, sb = fb.quantize_128x128(dev_bf16(w["b"]))
+        d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        one = torch.ones((), device="cuda")
+        ra, rb = torch.ones((M, 1), device="cuda"), torch.ones((1, N), device="cuda")
+        bt = b.t()
+        fns = {
+            "block_scaled_gemm": lambda: fb.gemm(a, sa, b, sb, out=d),
+            "hipblaslt_fp8_tensorwise": lambda: torch._scaled_mm(a, bt, scale_a=one, scale_b=one,
+                                                                 out_dtype=torch.bfloat16),
+            "hipblaslt_fp8_rowwise": lambda: torch._scaled_mm(a, bt, scale_a=ra, scale_b=rb,
+                                                              out_dtype=torch.bfloat16),
+        }
+        times = {k: [] for k in fns}
+        for f in fns.values():
+            for _ in range(3):
+                f()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            for k, f in fns.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(burst):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+                times[k].append(e0.elapsed_time(e1) * 1e3 / burst)
+        flops = 2.0 * M * N * K
+        out[f"{M}x{N}x{K}"] = {k: {"us": round(float(np.median(v)), 2),
+                                   "TFLOPs": round(flops / float(np.median(v)) / 1e6, 1)}
+                               for k, v in times.items()}
+    return out
+
+
 def cpu_baseline(synth, reps=2):
     """The CPU oracle on the same step: 1x128 quantization of the whole BF16
     activation and its GEMM against the quantized weight, run `reps` times,
@@ -286,6 +330,9 @@ def main():
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
+    ap.add_argument("--vs-hipblaslt", action="store_true",
+                    help="only time the block-scaled GEMM beside hipBLASLt's plain FP8 GEMM on the same operand "
+                         "bytes (context for the roofline fraction) and print that as one JSON line")
     args = ap.parse_args()
     global EAGER
     EAGER = args.eager
@@ -304,6 +351,10 @@ def main():
         return
 
     from fp8_block_scaled_04_amd import fp8bs as fb, synth
+
+    if args.vs_hipblaslt:
+        print(json.dumps({"vs_hipblaslt": vs_hipblaslt(fb, synth)}), flush=True)
+        return
 
     M, N, K = WORKLOAD["M"], WORKLOAD["N"], WORKLOAD["K"]
     w = synth.dense(M, N, K, seed=0)
