@@ -118,7 +118,7 @@ def run_masked(a, sa, b, sb, cnt, out_dtype=torch.bfloat16):
     (4, 256, 2112, 128, [1, 128, 129, 255]),
     (2, 64, 16, 512, [70, -3]),                      # counts outside [0, cap] are clamped
     (6, 256, 96, 640, None),                         # seeded uniform counts
-    # large-tile path (20 experts x 16 column tiles)
+    # the 128x256 masked-tile path (40 row tiles x 16 column tiles)
     (20, 256, 4096, 256, [0, 1, 255, 256, 129, 128, 0, 7, 200, 256, 64, 3, 0, 0, 250, 100, 31, 256, 17, 90]),
 ])
 def test_masked(G, cap, N, K, counts):
