@@ -130,13 +130,22 @@ __device__ __forceinline__ float row_max2(const float (&am)[2], int lane) {
 // ---------------------------------------------------------------------------
 constexpr int kQ1Tiles = 2;
 
+// fl32(x / ss).  With power-of-two scales r = 1/ss is exact (ss lies in
+// [2^-85, 2^120], so r is a normal power of two) and x * r rounds the same
+// real number x / ss once: one multiply gives the correctly rounded quotient,
+// subnormal results and signed zeros included.
+template <bool POW2>
+__device__ __forceinline__ float quot(float x, const TileScale& t) {
+  return POW2 ? x * t.r : div_rn(x, t.ss, t.r);
+}
+
 template <bool POW2, bool SCALED>
 __device__ __forceinline__ uint2 quantize8(uint4 v, const TileScale& t) {
   float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                 bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
   float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = div_rn(SCALED ? x[i] * t.sx : x[i], t.ss, t.r);
+  for (int i = 0; i < 8; ++i) y[i] = quot<POW2>(SCALED ? x[i] * t.sx : x[i], t);
   return make_uint2(pack4_e4m3(y[0], y[1], y[2], y[3]), pack4_e4m3(y[4], y[5], y[6], y[7]));
 }
 
@@ -198,14 +207,14 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(const uint16_t* __restri
 // the tile is one of those with amax < 2^-60, evaluated on x * 2^64.  The
 // callers branch on a wave-uniform flag, so the common case carries no
 // per-element multiply or select.
-template <bool SCALED>
+template <bool POW2, bool SCALED>
 __device__ __forceinline__ uint4 quantize16(const float (&x)[16], const TileScale& t) {
   uint32_t packed[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     float y[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = div_rn(SCALED ? x[4 * k + e] * t.sx : x[4 * k + e], t.ss, t.r);
+    for (int e = 0; e < 4; ++e) y[e] = quot<POW2>(SCALED ? x[4 * k + e] * t.sx : x[4 * k + e], t);
     packed[k] = pack4_e4m3(y[0], y[1], y[2], y[3]);
   }
   return make_uint4(packed[0], packed[1], packed[2], packed[3]);
@@ -228,7 +237,7 @@ __device__ __forceinline__ void requant_columns(const float (&d)[4][16], const f
       ts.ss = quad_bcast(mine.ss, j);
       ts.r = quad_bcast(mine.r, j);
       ts.sx = SC ? quad_bcast(mine.sx, j) : 1.0f;
-      nt_store16(qrow + j * ld, quantize16<SC>(d[j], ts));
+      nt_store16(qrow + j * ld, quantize16<POW2, SC>(d[j], ts));
     }
   };
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(mine.sx != 1.0f) != 0, 0))
