@@ -292,9 +292,66 @@ def cpu_baseline(synth, reps=2):
         a, sa = oq.quantize_1x128(w["a"])
         _ = og.gemm_ref(a, sa, bq, bs, "bf16")
     dt = (time.perf_counter() - t0) / reps
-    return dict(value=2 * M * N * K / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
+        pass
+    return dict(value=2 * M * N * K / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle", cpu_model=model,
                 sample=f"the whole step ({M}x{K} activation quantized 1x128, then its {M}x{N}x{K} GEMM, "
                        f"{2 * M * N * K / 1e9:.0f} GFLOP) run {reps} times: {dt:.2f} s per step")
+
+
+def smi_sample():
+    """Graphics clock (MHz, mean over the XCDs) and socket power (W) from
+    amd-smi, or None where the tool is missing or prints something else."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p"], capture_output=True, text=True, timeout=20)
+    except Exception:
+        return None
+    gfx, power, section = [], None, ""
+    for line in r.stdout.splitlines():
+        t = line.strip()
+        if t.endswith(":") and t[:-1].replace("_", "").isalnum():
+            section = t[:-1]
+        if t.startswith("SOCKET_POWER:"):
+            try:
+                power = float(t.split(":", 1)[1].split()[0])
+            except ValueError:
+                pass
+        if t.startswith("CLK:") and section.startswith("GFX_"):
+            try:
+                gfx.append(float(t.split(":", 1)[1].split()[0]))
+            except ValueError:
+                pass
+    if not gfx and power is None:
+        return None
+    return {"gfx_clock_mhz": round(sum(gfx) / len(gfx), 0) if gfx else None, "socket_power_w": power}
+
+
+def sustained_clock(step, seconds=2.0):
+    """amd-smi's graphics clock and socket power while the step runs
+    continuously for `seconds` (sampled once, after the first second)."""
+    import threading
+    out = {}
+    stop = threading.Event()
+
+    def sampler():
+        time.sleep(min(1.0, seconds / 2))
+        if not stop.is_set():
+            out["s"] = smi_sample()
+    th = threading.Thread(target=sampler)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    return out.get("s")
 
 
 def profile_traffic(path, sources):
@@ -420,6 +477,7 @@ def main():
             ms_graph = (time.perf_counter() - t0) / args.steps * 1e3
         except Exception as exc:
             print(f"graph capture failed ({exc})", file=sys.stderr)
+    clocks = None if args.eager else sustained_clock(step)
     flops = 2.0 * M * N * K
     achieved = flops / gemm_us / 1e6
     rec = {
@@ -437,7 +495,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "fp8 linear forward: quantize_1x128(A bf16 4096x7168) + block-scaled GEMM "
                                "4096x2112x7168, bf16 out", "M": M, "N": N, "K": K,
-                   "ms_per_step_graph_replay": ms_graph},
+                   "ms_per_step_graph_replay": ms_graph,
+                   "clocks_sustained_step": clocks},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP8_PEAK_TFLOPS,
                      "traffic": profile_traffic(GEMM_PROFILE, GEMM_SOURCES),

@@ -15,7 +15,7 @@
 // amax by DPP row reductions, no LDS except for the transpose.
 #include <type_traits>
 
-#include "device_common.h"
+#include "quant_common.h"
 #include "launch.h"
 
 namespace fp8bs {
@@ -30,6 +30,7 @@ namespace {
 // 89 us); cached loads of its input, or cached stores in the transposing
 // quantizers, were slower.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 nt_load16(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
@@ -314,12 +315,17 @@ __global__ __launch_bounds__(256) void k_quantize_t128x1(const uint8_t* __restri
   float d[4][16];
   float am[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < 16; ++i) {
+    // the four codes of the word, two per (exact) packed conversion
+    const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[i], false);
+    const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[i], true);
+    const float dec[4] = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      d[j][i] = e4m3_to_f32(wv[i], j) * rsv[i];
+      d[j][i] = dec[j] * rsv[i];
       am[j] = __builtin_fmaxf(am[j], __builtin_fabsf(d[j][i]));
     }
+  }
   requant_columns<POW2>(d, am, l, qt + (kb * 128 + 4 * c4) * M + mb * 128 + 16 * rg, M,
                         st + mb * K + kb * 128 + 4 * c4);
 }
