@@ -56,3 +56,63 @@ def test_graph_replays_match_eager(M, N, K):
         assert np.array_equal(d.view(torch.int16).cpu().numpy(), want_d), f"replay {rep}: gemm output"
         step()                       # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_graph_replays_quantizers_and_masked_gemm():
+    """The transposing quantizers and the masked grouped GEMM (device-side
+    counts) inside one captured graph: every replay equals the eager run."""
+    print("graph capture dual / transpose-requant / masked gemm", flush=True)
+    M, K = 256, 512
+    x = bf16_dev(synth.activation(M, K, seed=11)["a"])
+    G, cap, N, Km = 4, 128, 256, 384
+    w = synth.masked(G, cap, N, Km, seed=12)
+    am, sam = fp8bs.quantize_1x128(bf16_dev(w["a"].reshape(G * cap, Km)))
+    am = am.view(G, cap, Km)
+    sam = sam.view(Km // 128, G, cap).permute(1, 0, 2).contiguous()
+    bm, sbm = fp8bs.quantize_128x128(bf16_dev(w["b"]))
+    cnt = torch.tensor([0, 5, 128, 77], dtype=torch.int32, device="cuda")
+    outs = {
+        "q": torch.empty((M, K), dtype=torch.float8_e4m3fn, device="cuda"),
+        "s": torch.empty((K // 128, M), dtype=torch.float32, device="cuda"),
+        "qt": torch.empty((K, M), dtype=torch.float8_e4m3fn, device="cuda"),
+        "st": torch.empty((M // 128, K), dtype=torch.float32, device="cuda"),
+        "qt2": torch.empty((K, M), dtype=torch.float8_e4m3fn, device="cuda"),
+        "st2": torch.empty((M // 128, K), dtype=torch.float32, device="cuda"),
+        "dm": torch.zeros((G, cap, N), dtype=torch.bfloat16, device="cuda"),
+    }
+
+    def step():
+        q, s, qt, st = fp8bs.quantize_dual(x)
+        qt2, st2 = fp8bs.quantize_transpose_128x1(q, s)
+        for k, v in (("q", q), ("s", s), ("qt", qt), ("st", st), ("qt2", qt2), ("st2", st2)):
+            outs[k].copy_(v)
+        fp8bs.grouped_gemm_masked(am, sam, bm, sbm, cnt, out=outs["dm"])
+
+    def snapshot():
+        return {k: (v.view(torch.uint8) if v.dtype == torch.float8_e4m3fn else
+                    v.view(torch.int16) if v.dtype == torch.bfloat16 else v).cpu().numpy().copy()
+                for k, v in outs.items()}
+
+    step()
+    torch.cuda.synchronize()
+    want = snapshot()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for k, v in outs.items():
+            if k != "dm":       # rows past the counts keep their previous contents
+                v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for k in want:
+            assert np.array_equal(got[k], want[k]), f"replay {rep}: {k}"
+        step()
+        torch.cuda.synchronize()
