@@ -129,7 +129,26 @@ def extra_kernels(fb, synth):
     byt = 2 * M * K + 2 * M * K + 8 * (M * K // 128)
     out["quantize_dual_8192x7168"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
                                           frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
-    del xs, qs, x0
+    # References for the 1:1 read:write stream of the transpose-requantizer:
+    # the code-only 128x128 block transpose of the same 8192 x 7168 codes
+    # (same access pattern, no arithmetic) and a plain device copy of the
+    # same number of bytes.
+    sw = [torch.ones((1, M // 128, K // 128), device="cuda") for _ in range(R)]
+    it = iter(range(10 ** 9))
+
+    def code_transpose(i):
+        return fb.transpose_128x128(qs[i % R][0].view(1, M, K), sw[i % R])
+    us, how = time_graph(lambda: code_transpose(next(it)))
+    byt = 2 * M * K
+    out["reference_code_transpose_8192x7168"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
+                                                     frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
+    srcs = [torch.empty(M * K, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    dsts = [torch.empty(M * K, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    it = iter(range(10 ** 9))
+    us, how = time_graph(lambda: (lambda i: dsts[i % R].copy_(srcs[i % R]))(next(it)))
+    out["reference_device_copy_58.7MB"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
+                                               frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
+    del xs, qs, x0, sw, srcs, dsts
     torch.cuda.empty_cache()
 
     # decode-shaped GEMM 128 x 24576 x 1536 (power-of-two scales) + its quantizer
