@@ -373,11 +373,26 @@ def sustained_clock(step, seconds=2.0):
     return out.get("s")
 
 
+def code_hash(sources):
+    """First 16 hex digits of the SHA-256 of the kernel sources with comments,
+    trailing blanks and empty lines removed, so that a summary stays valid
+    across comment-only edits but not across any change to the code."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            for line in fh:
+                line = re.sub(r"//.*$", "", line).rstrip()
+                if line:
+                    h.update(line.encode() + b"\n")
+    return h.hexdigest()[:16]
+
+
 def profile_traffic(path, sources):
     """HBM-side bytes per launch of the dominant kernel, as recorded in a
-    rocprofv3 summary under profiles/, or None when the kernel's sources have
-    changed since the counters were taken (the summary stores their hash)."""
-    import hashlib
+    rocprofv3 summary under profiles/, or None when the kernel's code has
+    changed since the counters were taken (the summary stores its hash)."""
     try:
         text = open(os.path.join(ROOT, path)).read()
     except OSError:
@@ -386,11 +401,7 @@ def profile_traffic(path, sources):
     hs = [l.split(":", 1)[1].split()[0] for l in text.splitlines() if l.startswith("kernel_source_sha256_16:")]
     if not tb or not hs:
         return None
-    h = hashlib.sha256()
-    for f in sources:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return int(tb[0]) if h.hexdigest()[:16] == hs[0] else None
+    return int(tb[0]) if code_hash(sources) == hs[0] else None
 
 
 def main():

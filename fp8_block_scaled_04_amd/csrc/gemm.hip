@@ -30,14 +30,18 @@
 //     that have too few 256x256 tiles to fill 256 CUs.
 //   * A and B chunks (BM x 128 and BN x 128 bytes) and the chunk's scales are
 //     streamed straight from memory into LDS with buffer_load ... lds (no
-//     VGPR staging; the K offset is a scalar), two stages, in whole 128-byte
-//     rows with a swizzle that lets MFMA fragments read LDS at close to its
-//     full rate.  The DMA of the next
-//     chunk starts right after each step's barrier.  The small tile also
-//     double-buffers its MFMA fragments in registers; the large one holds
-//     half of its weight fragments at a time.
+//     VGPR staging; the K offset is a scalar), two or three stages, in whole
+//     128-byte rows with a swizzle that lets MFMA fragments read LDS at close
+//     to its full rate.  The DMA of a freed stage starts right after each
+//     step's barrier.  The 128x128 tile double-buffers its MFMA fragments in
+//     registers; the 256-wide tiles rotate their weight fragments through a
+//     small register ring, each read two MFMA rows ahead of its use.
+//   * Waves whose rows all lie past the valid rows (a masked expert's count,
+//     a ragged last tile) skip their MFMAs and only keep the DMA and barrier
+//     rhythm.
 //   * Workgroup ids are renumbered so that tiles sharing operand panels run
-//     on the same XCD (own L2), then walked in groups of GROUP_M tile rows.
+//     on the same XCD (own L2), then walked in groups of group_m tile rows
+//     (4 for 256-row tiles, 8 for 128-row tiles).
 #include "device_common.h"
 #include "launch.h"
 
