@@ -527,6 +527,12 @@ def main():
                                "4096x2112x7168, bf16 out", "M": M, "N": N, "K": K,
                    "ms_per_step_graph_replay": ms_graph,
                    "clocks_sustained_step": clocks},
+        # Other hardware, for context only: the pages report DeepGEMM reaching
+        # up to 1350 FP8 TFLOP/s on NVIDIA Hopper (page 4, "Deepseek
+        # veroeffentlicht Deepgemm", section "Schluesselmerkmale von DeepGemm";
+        # no shape given), so it is not a baseline for this workload.
+        "context_other_hardware": {"tflops": 1350, "hardware": "NVIDIA Hopper", "shape": "not stated",
+                                   "what": "peak FP8 GEMM throughput the surveyed pages report for DeepGEMM"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP8_PEAK_TFLOPS,
                      "traffic": profile_traffic(GEMM_PROFILE, GEMM_SOURCES),
