@@ -146,6 +146,22 @@ bool grid_fits(int64_t rows, int64_t N, int64_t groups) {
   return tiles < (int64_t(1) << 30);
 }
 
+// The GEMM kernels address a tile's operand panels (up to 256 rows of K
+// bytes) and a group's scale arrays through buffer descriptors with 31-bit
+// sizes and 32-bit offsets: each of those regions must stay below 2^31 bytes.
+// rows: rows of one group's activation-scale array (M, Mt or cap);
+// wscale_rows: rows of the weight scales ([K/128][N] for the weight gradient,
+// else the [N/128][K/128] block grid).
+bool buffers_fit(int64_t rows, int64_t N, int64_t K, bool per_row_weight_scales) {
+  constexpr int64_t kMax = 0x7FFFFFFF;
+  const int64_t KT = K / 128, NB = (N + 127) / 128;
+  if (K > kMax / 256) return false;                                  // a 256-row operand panel
+  if (rows > 0 && KT > kMax / 4 / rows) return false;                // activation scales
+  const int64_t ws = per_row_weight_scales ? N : NB;
+  if (ws > 0 && KT > kMax / 4 / ws) return false;                    // weight scales
+  return true;
+}
+
 }  // namespace
 
 fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, void* d,
@@ -153,7 +169,7 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const
                                         fp8bs_stream_t stream) {
   if (M < 0) return FP8BS_ERR_SHAPE;
   if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
-  if (!grid_fits(M, N, 1)) return FP8BS_ERR_SHAPE;
+  if (!grid_fits(M, N, 1) || !buffers_fit(M, N, K, false)) return FP8BS_ERR_SHAPE;
   if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (M == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, nullptr, false)) return e;
@@ -168,7 +184,7 @@ fp8bs_status fp8bs_gemm_fp8_wgrad(const uint8_t* a, const float* sa, const uint8
                                   int64_t M, int64_t N, int64_t K, int32_t accumulate, fp8bs_stream_t stream) {
   if (M < 0) return FP8BS_ERR_SHAPE;
   if (fp8bs_status e = gemm_common(N, K, FP8BS_OUT_FP32)) return e;
-  if (!grid_fits(M, N, 1)) return FP8BS_ERR_SHAPE;
+  if (!grid_fits(M, N, 1) || !buffers_fit(M, N, K, true)) return FP8BS_ERR_SHAPE;
   if (accumulate != 0 && accumulate != 1) return FP8BS_ERR_FLAGS;
   if (M == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, nullptr, false)) return e;
@@ -183,7 +199,7 @@ fp8bs_status fp8bs_grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa
                                                int64_t K, int32_t out_dtype, uint32_t flags, fp8bs_stream_t stream) {
   if (G < 0 || Mt < 0 || Mt % 128) return FP8BS_ERR_SHAPE;
   if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
-  if (!grid_fits(Mt, N, 1)) return FP8BS_ERR_SHAPE;
+  if (!grid_fits(Mt, N, 1) || !buffers_fit(Mt, N, K, false)) return FP8BS_ERR_SHAPE;
   if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (G == 0 || Mt == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, m_offsets, true)) return e;
@@ -199,7 +215,7 @@ fp8bs_status fp8bs_grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, co
                                            int64_t K, int32_t out_dtype, uint32_t flags, fp8bs_stream_t stream) {
   if (G < 0 || cap < 0) return FP8BS_ERR_SHAPE;
   if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
-  if (!grid_fits(cap, N, G)) return FP8BS_ERR_SHAPE;
+  if (!grid_fits(cap, N, G) || !buffers_fit(cap, N, K, false)) return FP8BS_ERR_SHAPE;
   if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (G == 0 || cap == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, masked_m, true)) return e;

@@ -187,7 +187,12 @@ fp8bs_status fp8bs_transpose_128x128(const uint8_t* q, const float* s,
  *   d  : [M][N], BF16 (out_dtype = FP8BS_OUT_BF16) or FP32 (FP8BS_OUT_FP32)
  *   flags : 0, or FP8BS_SCALE_POW2 (power-of-two scales applied by the
  *           matrix core; see the flags above)
- * Requires M >= 0, N >= 0, N % 16 == 0, K > 0, K % 128 == 0.
+ * Requires M >= 0, N >= 0, N % 16 == 0, K > 0, K % 128 == 0, and (the
+ * kernels address operand panels and scale arrays with 32-bit offsets)
+ * 256 * K < 2^31 and 4 * (K/128) * M < 2^31 and 4 * (K/128) * ceil(N/128)
+ * < 2^31; the grouped and weight-gradient calls apply the same limits to
+ * their own scale arrays (per group, with cap or Mt rows).  Larger problems
+ * return FP8BS_ERR_SHAPE.
  */
 fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa,
                                         const uint8_t* b, const float* sb,

@@ -200,3 +200,26 @@ def test_quantize_dual_validation(lib):
     assert f(FAKE, 128, 128, FAKE, FAKE, FAKE, MIS, 0, None) == ALIGN
     if NO_DEVICE:
         assert f(FAKE, 128, 128, FAKE, FAKE, FAKE, FAKE, 0, None) == DEVICE
+
+
+def test_gemm_rejects_sizes_beyond_32bit_addressing(lib):
+    # Operand panels (256 rows of K bytes) and scale arrays are addressed with
+    # 32-bit offsets in the kernels; larger problems are refused up front.
+    # (Only where no GPU is visible: a case that wrongly passed the checks
+    # would otherwise launch on the fake pointers.)
+    if not NO_DEVICE:
+        pytest.skip("argument-only checks run where no GPU is visible")
+    g = fn(lib, "fp8bs_gemm_fp8_blockscaled", [P] * 5 + [I64] * 3 + [I32, U32, P])
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 256, (1 << 23), 0, 0, None) == SHAPE      # 256*K = 2^31
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 22, 256, 1 << 17, 0, 0, None) == SHAPE    # 4*(K/128)*M = 2^32
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 1 << 28, 1 << 16, 0, 0, None) == SHAPE    # weight block scales
+    w = fn(lib, "fp8bs_gemm_fp8_wgrad", [P] * 5 + [I64] * 3 + [I32, P])
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 1 << 22, 1 << 17, 0, None) == SHAPE     # per-row weight scales
+    c = fn(lib, "fp8bs_grouped_gemm_fp8_contiguous", [P] * 6 + [I32, I64, I64, I64, I32, U32, P])
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1 << 22, 256, 1 << 17, 0, 0, None) == SHAPE
+    m = fn(lib, "fp8bs_grouped_gemm_fp8_masked", [P] * 6 + [I32, I64, I64, I64, I32, U32, P])
+    assert m(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, (1 << 23), 0, 0, None) == SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 256, (1 << 23) - 128, 0, 0, None) == SHAPE  # 4*(K/128)*M >= 2^31
+    # inside the limits: the arguments pass and the device check answers
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 17, 256, 1 << 17, 0, 0, None) == DEVICE   # 4*(K/128)*M = 2^29
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 2112, 7168, 0, 0, None) == DEVICE
