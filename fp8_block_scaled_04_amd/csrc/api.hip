@@ -37,6 +37,7 @@ fp8bs_status check_device() {
 fp8bs_status launched(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH; }
 
 constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxGridX = 0x7FFFFFFF;
 
 }  // namespace
 
@@ -60,7 +61,7 @@ int32_t fp8bs_abi_version(void) { return FP8BS_ABI_VERSION; }
 fp8bs_status fp8bs_quantize_1x128(const void* x, int64_t M, int64_t K, uint8_t* q, float* s, uint32_t flags,
                                   fp8bs_stream_t stream) {
   if (M < 0 || K <= 0 || K % 128) return FP8BS_ERR_SHAPE;
-  if ((K / 128 + 3) / 4 > kMaxGridY) return FP8BS_ERR_SHAPE;
+  if ((K / 128 + 3) / 4 > kMaxGridY || (M + 15) / 16 > kMaxGridX) return FP8BS_ERR_SHAPE;
   if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (M == 0) return FP8BS_OK;
   if (!x || !q || !s) return FP8BS_ERR_NULL;
@@ -73,7 +74,7 @@ fp8bs_status fp8bs_quantize_1x128(const void* x, int64_t M, int64_t K, uint8_t* 
 fp8bs_status fp8bs_quantize_transpose_128x1(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt,
                                             float* st, uint32_t flags, fp8bs_stream_t stream) {
   if (M < 0 || K < 0 || M % 128 || K % 128) return FP8BS_ERR_SHAPE;
-  if (K / 128 > kMaxGridY) return FP8BS_ERR_SHAPE;
+  if (K / 128 > kMaxGridY || M / 128 > kMaxGridX) return FP8BS_ERR_SHAPE;
   if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (M == 0 || K == 0) return FP8BS_OK;
   if (!q || !s || !qt || !st) return FP8BS_ERR_NULL;
@@ -86,7 +87,7 @@ fp8bs_status fp8bs_quantize_transpose_128x1(const uint8_t* q, const float* s, in
 fp8bs_status fp8bs_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t K, uint8_t* q, float* s,
                                     uint32_t flags, fp8bs_stream_t stream) {
   if (G < 0 || N < 0 || K <= 0 || K % 128) return FP8BS_ERR_SHAPE;
-  if (G > kMaxGridY || K / 128 > kMaxGridY) return FP8BS_ERR_SHAPE;
+  if (G > kMaxGridY || K / 128 > kMaxGridY || (N + 127) / 128 > kMaxGridX) return FP8BS_ERR_SHAPE;
   if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (G == 0 || N == 0) return FP8BS_OK;
   if (!w || !q || !s) return FP8BS_ERR_NULL;
@@ -99,7 +100,7 @@ fp8bs_status fp8bs_quantize_128x128(const void* w, int64_t G, int64_t N, int64_t
 fp8bs_status fp8bs_quantize_dual(const void* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt, float* st,
                                 uint32_t flags, fp8bs_stream_t stream) {
   if (M < 0 || K < 0 || M % 128 || K % 128) return FP8BS_ERR_SHAPE;
-  if (K / 128 > kMaxGridY || M / 128 > (int64_t)0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (K / 128 > kMaxGridY || M / 128 > kMaxGridX) return FP8BS_ERR_SHAPE;
   if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (M == 0 || K == 0) return FP8BS_OK;
   if (!x || !q || !s || !qt || !st) return FP8BS_ERR_NULL;
@@ -112,7 +113,7 @@ fp8bs_status fp8bs_quantize_dual(const void* x, int64_t M, int64_t K, uint8_t* q
 fp8bs_status fp8bs_transpose_128x128(const uint8_t* q, const float* s, int64_t G, int64_t N, int64_t K, uint8_t* qt,
                                     float* st, fp8bs_stream_t stream) {
   if (G < 0 || N < 0 || N % 16 || K < 0 || K % 128) return FP8BS_ERR_SHAPE;
-  if (G > kMaxGridY || K / 128 > kMaxGridY) return FP8BS_ERR_SHAPE;
+  if (G > kMaxGridY || K / 128 > kMaxGridY || (N + 127) / 128 > kMaxGridX) return FP8BS_ERR_SHAPE;
   if (G == 0 || N == 0 || K == 0) return FP8BS_OK;
   if (!q || !s || !qt || !st) return FP8BS_ERR_NULL;
   if (!aligned16(q) || !aligned16(qt) || (reinterpret_cast<uintptr_t>(s) & 3u) ||
