@@ -192,6 +192,50 @@ __device__ __forceinline__ void group_rows(const int32_t* offs, int g, int64_t m
   hi = hi < lo ? lo : (hi > mt ? mt : hi);
 }
 
+// Per-group tile counts c(g) of the masked layout, one group per lane and
+// 64 groups per pass: one vector load (or two) per pass instead of a
+// dependent scalar load per group (walking 32 experts that way took a
+// median 6.6 us per workgroup before its first DMA).  Every lane of the
+// wave must be active.  group_total returns the sum over all G groups;
+// group_find the group g holding unit x (units counted in group order, x
+// below the total) and, in `first`, the number of units before g (G if x is
+// not below the total).
+template <class F>
+__device__ __forceinline__ int group_total(int G, F c) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    int v = g0 + lane < G ? c(g0 + lane) : 0;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    total += v;
+  }
+  return total;
+}
+template <class F>
+__device__ __forceinline__ int group_find(int G, F c, int x, int& first) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int v = g0 + lane < G ? c(g0 + lane) : 0;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(incl, d);
+      if (lane >= d) incl += u;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > x);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      first = base + __builtin_amdgcn_readlane(incl - v, l);
+      return g0 + l;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  first = base;
+  return G;
+}
+
 struct GemmArgs {
   const uint8_t* a;
   const float* sa;
@@ -236,20 +280,16 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int64_t K, int KT, i
   t.d_row0 = 0;
   if constexpr (MODE == kMasked) {
     // Tiles in group order; within a group, m fastest.
-    int total = 0;
-    for (int gg = 0; gg < p.G; ++gg) total += (int)((masked_count(p.groups[gg], p.M) + BM - 1) / BM);
-    total *= p.tiles_n;
+    auto tiles_of = [&](int gg) { return (int)((masked_count(p.groups[gg], p.M) + BM - 1) / BM) * p.tiles_n; };
+    const int total = group_total(p.G, tiles_of);
     int pid = xcd_remap((int)blockIdx.x, total);
     if (pid < 0) return false;
-    int g = 0, cnt = 0;
-    int64_t rows = 0;
-    for (; g < p.G; ++g) {
-      rows = masked_count(p.groups[g], p.M);
-      cnt = (int)((rows + BM - 1) / BM) * p.tiles_n;
-      if (pid < cnt) break;
-      pid -= cnt;
-    }
-    const int tcnt = cnt / p.tiles_n;
+    int first = 0;
+    const int g = group_find(p.G, tiles_of, pid, first);
+    if (g >= p.G) return false;
+    pid -= first;
+    const int64_t rows = masked_count(p.groups[g], p.M);
+    const int tcnt = (int)((rows + BM - 1) / BM);
     const int tn = pid / tcnt, tm = pid - tn * tcnt;
     t.m0 = (int64_t)tm * BM;
     t.n0 = (int64_t)tn * BN;
@@ -263,6 +303,9 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int64_t K, int KT, i
     // Dense: the grid is exact.  Contiguous: tile t of group g has index
     // (tiles of the groups before g) + t (group boundaries are multiples of
     // 128 rows, so a tile never spans two groups).
+    // (Contiguous layouts have few groups -- one per expert of the GPU -- and
+    // walk them in order; the lane-parallel lookup measured 4 % slower on 8
+    // groups.)
     int tiles_m = p.tiles_m;
     if (MODE == kContiguous) {
       tiles_m = 0;
