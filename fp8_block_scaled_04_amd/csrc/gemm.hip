@@ -281,12 +281,29 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int64_t K, int KT, i
   if constexpr (MODE == kMasked) {
     // Tiles in group order; within a group, m fastest.
     auto tiles_of = [&](int gg) { return (int)((masked_count(p.groups[gg], p.M) + BM - 1) / BM) * p.tiles_n; };
-    const int total = group_total(p.G, tiles_of);
-    int pid = xcd_remap((int)blockIdx.x, total);
-    if (pid < 0) return false;
-    int first = 0;
-    const int g = group_find(p.G, tiles_of, pid, first);
-    if (g >= p.G) return false;
+    int pid, g, first = 0;
+    if (p.G <= 64) {
+      // One load and one scan serve both the total and the search.
+      const int lane = threadIdx.x & 63;
+      const int v = lane < p.G ? tiles_of(lane) : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(incl, d);
+        if (lane >= d) incl += u;
+      }
+      pid = xcd_remap((int)blockIdx.x, __builtin_amdgcn_readlane(incl, 63));
+      if (pid < 0) return false;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > pid);
+      if (!hit) return false;
+      g = __builtin_ctzll(hit);
+      first = __builtin_amdgcn_readlane(incl - v, g);
+    } else {
+      pid = xcd_remap((int)blockIdx.x, group_total(p.G, tiles_of));
+      if (pid < 0) return false;
+      g = group_find(p.G, tiles_of, pid, first);
+      if (g >= p.G) return false;
+    }
     pid -= first;
     const int64_t rows = masked_count(p.groups[g], p.M);
     const int tcnt = (int)((rows + BM - 1) / BM);
