@@ -120,6 +120,13 @@ def run_masked(a, sa, b, sb, cnt, out_dtype=torch.bfloat16):
     (6, 256, 96, 640, None),                         # seeded uniform counts
     # the 128x256 masked-tile path (40 row tiles x 16 column tiles)
     (20, 256, 4096, 256, [0, 1, 255, 256, 129, 128, 0, 7, 200, 256, 64, 3, 0, 0, 250, 100, 31, 256, 17, 90]),
+    # the masked tile's three-stage pipeline with K of exactly three chunks,
+    # then with a chunk count that is not a multiple of three (counts 1, 64,
+    # 129 leave whole waves without rows)
+    (20, 256, 6144, 384, [0, 1, 255, 256, 129, 128, 0, 7, 200, 256, 64, 3, 0, 0, 250, 100, 31, 256, 17, 90]),
+    (24, 256, 4096, 640, None),
+    (64, 128, 2048, 512, None),                      # the most groups the one-wave expert lookup holds
+    (65, 128, 2048, 384, None),                      # one more: the lookup in passes of 64 groups
 ])
 def test_masked(G, cap, N, K, counts):
     print(f"masked G={G} cap={cap} N={N} K={K} counts={counts}", flush=True)
@@ -133,8 +140,11 @@ def test_masked(G, cap, N, K, counts):
         assert_gemm_close(out_host_f64(out)[valid], ref_b, "masked")
 
 
-def test_masked_fp32_out():
-    a, sa, b, sb, cnt = masked_operands(2, 128, 32, 256, seed=5, counts=[50, 128])
+@pytest.mark.parametrize("G,cap,N,K,counts", [(2, 128, 32, 256, [50, 128]),
+                                              (12, 256, 8192, 512, [256, 0, 70, 129, 1, 255, 128, 64, 65, 0, 200, 3])])
+def test_masked_fp32_out(G, cap, N, K, counts):
+    print(f"masked fp32 G={G} cap={cap} N={N} K={K}", flush=True)
+    a, sa, b, sb, cnt = masked_operands(G, cap, N, K, seed=5, counts=counts)
     out = run_masked(a, sa, b, sb, cnt, torch.float32)
     ref = gemm.grouped_masked_f64(a, sa, b, sb, cnt)
     valid = ~np.isnan(ref[:, :, 0])

@@ -125,6 +125,9 @@ def test_pow2_contiguous():
 
 @pytest.mark.parametrize("G,cap,N,K,counts", [(3, 256, 96, 256, [0, 256, 77]),
                                               (20, 256, 4096, 256, [0, 1, 255, 256, 129, 128, 0, 7, 200, 256, 64,
+                                                                    3, 0, 0, 250, 100, 31, 256, 17, 90]),
+                                              # hardware scaling on the masked tile, K of four chunks
+                                              (20, 256, 6144, 512, [0, 1, 255, 256, 129, 128, 0, 7, 200, 256, 64,
                                                                     3, 0, 0, 250, 100, 31, 256, 17, 90])])
 def test_pow2_masked(G, cap, N, K, counts):
     print(f"pow2 masked G={G} cap={cap} N={N} K={K}", flush=True)
