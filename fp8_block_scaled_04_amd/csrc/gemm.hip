@@ -27,7 +27,8 @@
 //     load at most ~300 bytes per MFMA to keep the matrix cores busy.  A
 //     256x256 tile loads 256 bytes per MFMA (8 waves, two per SIMD, wave tile
 //     64x128); 128x128 (4 waves, 64x64 each) loads 512 and serves the shapes
-//     that have too few 256x256 tiles to fill 256 CUs.
+//     that have too few 256x256 tiles to fill 256 CUs, as do 256x160 (8 waves
+//     of 64x80) and 192x192 (12 waves of 64x48, three per SIMD).
 //   * A and B chunks (BM x 128 and BN x 128 bytes) and the chunk's scales are
 //     streamed straight from memory into LDS with buffer_load ... lds (no
 //     VGPR staging; the K offset is a scalar), two or three stages, in whole
@@ -41,7 +42,7 @@
 //     rhythm.
 //   * Workgroup ids are renumbered so that tiles sharing operand panels run
 //     on the same XCD (own L2), then walked in groups of group_m tile rows
-//     (4 for 256-row tiles, 8 for 128-row tiles).
+//     (4 for 256-row tiles, 8 for the smaller ones).
 #include "device_common.h"
 #include "launch.h"
 
@@ -100,6 +101,13 @@ using LargeTile = Cfg<256, 256, 4, 2, false>;
 // 83 us with cold caches; two stages for the weight gradient.
 using MidTile = Cfg<256, 160, 4, 2, false, 3, true>;
 using WgradMidTile = Cfg<256, 160, 4, 2, false>;
+// 192x192 with 12 waves (3x4, 64x48 each: three waves per SIMD), three
+// stages, compact scales (147 KB of LDS).  On 4096x2112x7168 it makes 242
+// tiles of 10 % less work than the 224 of 256x160 and hides more latency
+// with its third wave per SIMD: 69.7 -> 65.2 us on random codes, 66.0 ->
+// 57.8 us on zero codes (interleaved A/B; outputs bit-identical).  One wave
+// per SIMD (256x160 as 4 waves of 64x160) was far slower (109 us).
+using Tile192 = Cfg<192, 192, 3, 4, false, 3, true>;
 // Memory-bound shapes (few rows): 128x96 tiles, three stages, one
 // workgroup per CU on the 24576-column decode projection.
 using StreamTile = Cfg<128, 96, 2, 2, false, 3>;
@@ -950,8 +958,8 @@ hipError_t launch_cfg(const GemmProblem& pr, hipStream_t stream) {
   // covers fewer activation rows and more weight rows (4096x2112x7168 on
   // 256x160 tiles: 4 x 7 instead of 8 x 3.5 tiles, 15.3 instead of 19.3 MB
   // of operands per L2; 1-3 % faster on the dense and weight-gradient
-  // shapes, interleaved A/B); the 128-row tiles keep 8 (4 made the
-  // contiguous MoE shape 10 % slower).
+  // shapes, interleaved A/B); the smaller tiles keep 8 (4 made the
+  // contiguous MoE shape on 128-row tiles 10 % slower).
   a.group_m = C::BM >= 256 ? 4 : 8;
   a.accumulate = pr.accumulate ? 1 : 0;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * (MODE == kMasked ? pr.G : 1);
@@ -976,8 +984,9 @@ hipError_t launch_cfg(const GemmProblem& pr, hipStream_t stream) {
 // shape takes ceil(tiles per XCD / workgroup slots per XCD) rounds, each
 // costing about the time of one tile.  Relative tile costs (measured on
 // dense 8192x4096x7168): 256x256 = 1, 256x160 = 0.7, 128x128 at two
-// workgroups per CU = 0.52.  The 256x256 tile loads the fewest operand bytes
-// per MFMA and wins whenever it fills the chip.
+// workgroups per CU = 0.52; 192x192 = 0.65 (against 256x160 on
+// 4096x2112x7168).  The 256x256 tile loads the fewest operand bytes per MFMA
+// and wins whenever it fills the chip.
 template <class C>
 double est_rounds(int64_t tiles, double cost) {
   const int64_t per_xcd = (tiles + 7) / 8;
@@ -994,28 +1003,34 @@ hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
                                  ((p.N + MaskedTile::BN - 1) / MaskedTile::BN);
     if (masked_tiles >= 256) return launch_cfg<MaskedTile, MODE>(p, stream);
     return launch_cfg<SmallTile, MODE>(p, stream);
-  }
-  // Few rows (decode): the weights stream from HBM once; a deep pipeline
-  // over many small tiles keeps enough bytes in flight.
-  if constexpr (MODE == kDense) {
-    if (p.M <= 128) return launch_cfg<StreamTile, MODE>(p, stream);
-  }
-  // Row tiles: dense exact; contiguous counts on average half a partial tile
-  // per group.
-  auto mtiles = [&](int64_t bm) {
-    return MODE == kContiguous ? p.M / bm + (p.G + 1) / 2 : (p.M + bm - 1) / bm;
-  };
-  const double t_large = est_rounds<LargeTile>(mtiles(256) * ((p.N + 255) / 256), 1.0);
-  const double t_mid = est_rounds<MidTile>(mtiles(256) * ((p.N + 159) / 160), 0.7);
-  const double t_small = est_rounds<SmallTile>(mtiles(128) * ((p.N + 127) / 128), 0.52);
-  if constexpr (MODE == kWgrad) {
-    // per-row weight scales are read in the 256-wide tiles' loop only
-    if (t_large <= t_mid) return launch_cfg<LargeTile, MODE>(p, stream);
-    return launch_cfg<WgradMidTile, MODE>(p, stream);
   } else {
-    if (t_large <= t_mid && t_large <= t_small) return launch_cfg<LargeTile, MODE>(p, stream);
-    if (t_mid <= t_small) return launch_cfg<MidTile, MODE>(p, stream);
-    return launch_cfg<SmallTile, MODE>(p, stream);
+    // Few rows (decode): the weights stream from HBM once; a deep pipeline
+    // over many small tiles keeps enough bytes in flight.
+    if constexpr (MODE == kDense) {
+      if (p.M <= 128) return launch_cfg<StreamTile, MODE>(p, stream);
+    }
+    // Row tiles: dense exact; contiguous counts on average half a partial
+    // tile per group.
+    auto mtiles = [&](int64_t bm) {
+      return MODE == kContiguous ? p.M / bm + (p.G + 1) / 2 : (p.M + bm - 1) / bm;
+    };
+    const double t_large = est_rounds<LargeTile>(mtiles(256) * ((p.N + 255) / 256), 1.0);
+    const double t_mid = est_rounds<MidTile>(mtiles(256) * ((p.N + 159) / 160), 0.7);
+    const double t_small = est_rounds<SmallTile>(mtiles(128) * ((p.N + 127) / 128), 0.52);
+    if constexpr (MODE == kWgrad) {
+      // per-row weight scales are read in the 256-wide tiles' loop only
+      if (t_large <= t_mid) return launch_cfg<LargeTile, MODE>(p, stream);
+      return launch_cfg<WgradMidTile, MODE>(p, stream);
+    } else {
+      const double t_192 = est_rounds<Tile192>(mtiles(192) * ((p.N + 191) / 192), 0.65);
+      if (t_large <= t_mid && t_large <= t_192 && t_large <= t_small) return launch_cfg<LargeTile, MODE>(p, stream);
+      // (on a tie the 128x128 tile: contiguous groups are multiples of 128
+      // rows, so their partial 192-row tiles waste more; 8x8192x4096x7168
+      // measured 265 us on 128x128 against 273 us on 192x192)
+      if (t_192 <= t_mid && t_192 < t_small) return launch_cfg<Tile192, MODE>(p, stream);
+      if (t_mid <= t_small) return launch_cfg<MidTile, MODE>(p, stream);
+      return launch_cfg<SmallTile, MODE>(p, stream);
+    }
   }
 }
 

@@ -38,7 +38,9 @@ def run(a, sa, b, sb, out_dtype=torch.bfloat16):
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (1, 16, 128), (37, 48, 384), (130, 2112, 256),
                                    (256, 272, 1024), (64, 4096, 128), (300, 400, 640), (513, 144, 1152),
                                    # enough 256x256 tiles for the large-tile path; ragged edges
-                                   (4096, 4096, 256), (4000, 4112, 384)])
+                                   (4096, 4096, 256),
+                                   # the 192x192 tile (ragged edges), then the 256x160 tile
+                                   (4000, 4112, 384), (2304, 4096, 256), (2560, 3584, 384)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_gemm_workload_recipe(M, N, K, out_dtype):
     print(f"gemm M={M} N={N} K={K} out={out_dtype}", flush=True)
@@ -52,8 +54,9 @@ def test_gemm_workload_recipe(M, N, K, out_dtype):
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("M,N,K", [(256, 272, 1024),
-                                   # 256x160 tiles: a wave's columns straddle two weight blocks
-                                   (4000, 4112, 256)])
+                                   # 192x192 and 256x160 tiles: a wave's columns straddle two
+                                   # weight blocks
+                                   (4000, 4112, 256), (2560, 3584, 256)])
 def test_gemm_exact_integer_inputs_bit_exact(M, N, K, out_dtype):
     # codes with integer values in [-16, 16] and power-of-two scales: every
     # partial sum is exact in FP32, so the output is the one rounding of the
