@@ -49,6 +49,9 @@ def run_contiguous(a, sa, b, sb, offs, Mt, N):
     (2, 256, 16, 384, [0, 0, 0]),                    # every group empty
     # large-tile path: 128-row groups end in half tiles, one group is empty
     (7, 4608, 4096, 256, [0, 128, 128, 1152, 2304, 2432, 3840, 4480]),
+    # the 192x192 tile: groups of 640 and 1280 rows end inside a tile, rows
+    # 1920.. unused
+    (2, 2048, 4096, 256, [0, 640, 1920]),
 ])
 def test_contiguous(G, Mt, N, K, offsets):
     print(f"contiguous G={G} Mt={Mt} N={N} K={K} offs={offsets}", flush=True)
