@@ -453,11 +453,12 @@ def main():
         q, s = fb.quantize_1x128(x)
         fb.gemm(q, s, bq, bs, out=d)
 
-    # The GEMM's own duration (roofline): HIP events, on the stream it runs
-    # on, around bursts of 10 back-to-back launches right after the step's
-    # quantizer.  (An event between two kernels adds a drain to the interval:
-    # one event pair per launch read 88-90 us where the kernel trace shows
-    # 78 us.)
+    # The GEMM's own duration, second reading: HIP events, on the stream it
+    # runs on, around bursts of 10 back-to-back launches right after one of
+    # the step's quantizer calls.  (An event between two kernels adds a drain
+    # to the interval: one event pair per launch read 88-90 us where the
+    # kernel trace shows 78 us.)  A burst of GEMMs alone draws more power than
+    # the step, so it runs at a lower clock.
     for _ in range(args.warmup):
         step()
     burst = 10
@@ -472,16 +473,34 @@ def main():
         e1.record()
         spans.append((e0, e1))
     torch.cuda.synchronize()
-    gemm_us = float(np.mean([a.elapsed_time(b) for a, b in spans])) * 1e3 / burst
+    gemm_us_burst = float(np.mean([a.elapsed_time(b) for a, b in spans])) * 1e3 / burst
     # The timed steps: plain launches, exactly `steps` of them between two
-    # synchronizations (nothing else in flight).
+    # synchronizations (nothing else in flight), bracketed by HIP events on
+    # the launch stream as well.
     torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record()
     for _ in range(args.steps):
         step()
+    ev1.record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt / args.steps * 1e3
+    # The GEMM's duration inside the timed steps (roofline): the events' span
+    # of the steps minus that of the same number of quantizer calls alone,
+    # per step -- the GEMM under the step's own power state.
+    qv0, qv1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qv0.record()
+    for _ in range(args.steps):
+        fb.quantize_1x128(x)
+    qv1.record()
+    torch.cuda.synchronize()
+    quant_us = qv0.elapsed_time(qv1) * 1e3 / args.steps
+    gemm_us = ev0.elapsed_time(ev1) * 1e3 / args.steps - quant_us
+    kernel_us_method = "timed steps minus as many quantizer calls, HIP events"
+    if not gemm_us > 0:   # the difference of two noisy spans; not expected
+        gemm_us, kernel_us_method = gemm_us_burst, "bursts of 10 launches, HIP events"
 
     # For reference, the same step captured once in a HIP graph and replayed
     # (the library launches kernels only).  On ROCm 7.2 the replays were
@@ -536,7 +555,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP8_PEAK_TFLOPS,
                      "traffic": profile_traffic(GEMM_PROFILE, GEMM_SOURCES),
-                     "kernel": "k_gemm (dense)", "kernel_us": gemm_us},
+                     "kernel": "k_gemm (dense)", "kernel_us": gemm_us,
+                     "kernel_us_method": kernel_us_method,
+                     "kernel_us_burst": gemm_us_burst, "quantizer_us_in_step": quant_us},
     }
     if not args.no_extra:
         rec["kernels"] = extra_kernels(fb, synth)
