@@ -43,10 +43,11 @@ def ref_out(a, sa, b, sb, out_dtype):
             else gemm.round_out(r, "f32")).astype(np.float64)
 
 
-# shapes that reach every tile: 128x128 (double-buffered), 256x160, 256x256,
-# 128x96 (few rows), with ragged edges
+# shapes that reach every tile: 128x128 (double-buffered), 192x192 (4096x2112,
+# 4000x4112), 256x160 (2450x3696), 256x256, 128x96 (few rows), with ragged edges
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (37, 48, 384), (300, 400, 640), (4096, 2112, 1024),
-                                   (4096, 4096, 256), (4000, 4112, 384), (128, 24576, 1536), (1, 16, 128)])
+                                   (4096, 4096, 256), (4000, 4112, 384), (2450, 3696, 256), (128, 24576, 1536),
+                                   (1, 16, 128)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_pow2_recipe(M, N, K, out_dtype):
     print(f"pow2 gemm M={M} N={N} K={K} out={out_dtype}", flush=True)
