@@ -61,7 +61,7 @@ int32_t fp8bs_abi_version(void) { return FP8BS_ABI_VERSION; }
 fp8bs_status fp8bs_quantize_1x128(const void* x, int64_t M, int64_t K, uint8_t* q, float* s, uint32_t flags,
                                   fp8bs_stream_t stream) {
   if (M < 0 || K <= 0 || K % 128) return FP8BS_ERR_SHAPE;
-  if ((K / 128 + 3) / 4 > kMaxGridY || (M + 15) / 16 > kMaxGridX) return FP8BS_ERR_SHAPE;
+  if ((K / 128 + fp8bs::kQ1Tiles - 1) / fp8bs::kQ1Tiles > kMaxGridY || (M + 15) / 16 > kMaxGridX) return FP8BS_ERR_SHAPE;
   if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (M == 0) return FP8BS_OK;
   if (!x || !q || !s) return FP8BS_ERR_NULL;

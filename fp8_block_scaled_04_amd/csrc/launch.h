@@ -7,6 +7,10 @@
 
 namespace fp8bs {
 
+// 1x128 tiles of one row handled by one lane of k_quantize_1x128 (the grid's
+// y dimension is ceil(K/128 / kQ1Tiles)); the C ABI bounds that grid with it.
+constexpr int kQ1Tiles = 2;
+
 hipError_t launch_quantize_1x128(const void* x, int64_t M, int64_t K, uint8_t* q, float* s, bool pow2,
                                  hipStream_t stream);
 hipError_t launch_quantize_t128x1(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt, float* st,

@@ -51,11 +51,14 @@ __device__ __forceinline__ float row16_max(float v) {
 // Writing the residual with its sign flipped keeps the sign of a zero
 // quotient (x = -0 gives -0) without a separate copysign.  Tiles with
 // amax < 2^-60 are evaluated on x * 2^64 and s * 2^64 (both exact), which
-// keeps every operand normal; quotients that still come out subnormal encode
-// to a zero E4M3 code either way.  The resulting E4M3 codes, sign included,
-// were compared against enc(x / s) for every pair of BF16 (x, amax) with
-// |x| <= amax and both signs of x, for all power-of-two scales, and for 4e8
-// random FP32 pairs: no difference.
+// keeps every operand normal.  Where the correction's preconditions still
+// fail (a residual that underflows: |x| < 2^-102 on the unscaled path, or a
+// subnormal quotient) both the result and the true quotient are at most
+// 2^-10 with the same sign, so both encode to the E4M3 zero of that sign.
+// tests/test_quant_divide.py replays these operations on the CPU for every
+// pair of BF16 (x, amax) with |x| <= amax, both signs, with and without
+// power-of-two scales; tests/test_gpu_exhaustive.py runs one tile per BF16
+// amax through the kernels.
 struct TileScale {
   float s;    // the scale written to memory
   float ss;   // s * sx
@@ -99,10 +102,13 @@ __device__ __forceinline__ float div_rn(float x, float s, float r) {
 // values into one dword, byte i = value i.
 //
 // pack4_e4m3 is for the quantizers, whose values satisfy |y| <= 448 * (1 +
-// 2^-22) < 464: the conversion rounds everything in [448, 464] to 448
-// (checked on the GPU for every FP32 value in that range), so no clamp is
-// needed.  pack4_e4m3_sat clamps to +-448 first (satfinite) for arbitrary
-// finite inputs.
+// 2^-22) < 464 (x / s with s = RN(amax / 448) exceeds 448 only when the
+// scale rounded down): round to nearest even maps everything in [448, 464)
+// to 448, so no clamp is needed (every BF16 amax, about half of them with a
+// scale that rounded down, is checked bit-exact in
+// tests/test_gpu_exhaustive.py).  pack4_e4m3_sat clamps to +-448 first
+// (satfinite) for arbitrary inputs; the cast is compared with the oracle on
+// all 2^32 FP32 bit patterns there.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float clamp448(float y) {
   return __builtin_fminf(__builtin_fmaxf(y, -kE4M3Max), kE4M3Max);

@@ -129,7 +129,6 @@ __device__ __forceinline__ float row_max2(const float (&am)[2], int lane) {
 // row so that kQ1Tiles loads are in flight before any arithmetic.  Scales of 16
 // consecutive rows are written together (s is [K/128][M], M contiguous).
 // ---------------------------------------------------------------------------
-constexpr int kQ1Tiles = 2;
 
 // fl32(x / ss).  With power-of-two scales r = 1/ss is exact (ss lies in
 // [2^-85, 2^120], so r is a normal power of two) and x * r rounds the same

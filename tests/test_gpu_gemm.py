@@ -102,19 +102,16 @@ def test_gemm_writes_only_its_output():
     assert_gemm_close(out_host_f64(out), ref, "in-place out")
 
 
-def test_gemm_training_projection_full_size_sampled():
+def test_gemm_training_projection_full_size():
     # 4096 x 2112 x 7168: the last 128-wide column tile holds only 64 valid
-    # columns (ragged weight block).  Sampled rows x columns, incl. the tails.
+    # columns (ragged weight block).  Every output against the float64
+    # definition, rms over all of them.
     M, N, K = 4096, 2112, 7168
     print("gemm full size 4096x2112x7168", flush=True)
     a, sa, b, sb = operands(M, N, K, seed=0)
     d = run(a, sa, b, sb)
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(M - 16, M), rng.integers(0, M, 96)]))
-    cols = np.unique(np.concatenate([np.arange(0, 16), np.arange(N - 80, N), rng.integers(0, N, 160)]))
-    ref = bf16.to_f32(bf16.from_f64_rne(gemm.gemm_block_f64(a, sa, b, sb, rows, cols))).astype(np.float64)
-    got = out_host_f64(d)[np.ix_(rows, cols)]
-    assert_gemm_close(got, ref, "gemm 4096x2112x7168")
+    ref = bf16.to_f32(gemm.gemm_ref(a, sa, b, sb)).astype(np.float64)
+    assert_gemm_close(out_host_f64(d), ref, "gemm 4096x2112x7168")
 
 
 def test_gemm_decode_shape_pow2_full():

@@ -86,10 +86,11 @@ def test_data_gradient_chain(T, NO, NI):
     assert_gemm_close(out_host_f64(dx), ref, f"dgrad {T}x{NI}x{NO}")
 
 
-def test_data_gradient_projection_size_sampled():
-    # dX[4096][7168] = dY[4096][2112] W[2112][7168]: K padded to 2176
+def test_data_gradient_projection_size():
+    # dX[4096][7168] = dY[4096][2112] W[2112][7168]: K padded to 2176; every
+    # output against the float64 definition
     T, NO, NI = 4096, 2112, 7168
-    print("dgrad 4096x7168 (K 2112 -> 2176) sampled", flush=True)
+    print("dgrad 4096x7168 (K 2112 -> 2176)", flush=True)
     w = synth.dense(T, NO, NI, seed=11)["b"]
     dy = synth.activation(T, NO, seed=12)["a"]
     a, sa, qt, st = dgrad_operands_gpu(dy, w)
@@ -98,8 +99,5 @@ def test_data_gradient_projection_size_sampled():
     ra, rsa, rqt, rst = dgrad_operands_oracle(dy, w)
     assert_codes_equal(codes_host(qt), rqt, "W^T codes")
     assert_codes_equal(codes_host(a), ra, "dY codes")
-    rng = np.random.default_rng(13)
-    rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 48)]))
-    cols = np.unique(np.concatenate([[0, NI - 1], rng.integers(0, NI, 64)]))
-    ref = bf16.to_f32(bf16.from_f64_rne(gemm.gemm_block_f64(ra, rsa, rqt, rst, rows, cols))).astype(np.float64)
-    assert_gemm_close(out_host_f64(dx)[np.ix_(rows, cols)], ref, "dgrad sampled")
+    ref = bf16.to_f32(gemm.gemm_ref(ra, rsa, rqt, rst)).astype(np.float64)
+    assert_gemm_close(out_host_f64(dx), ref, "dgrad 4096x7168x2176")

@@ -69,17 +69,14 @@ def test_wgrad_exact_integer_bit_exact(M, N, K):
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
-def test_wgrad_projection_size_sampled():
-    # dW of the 7168 -> 2112 projection over 4096 tokens, sampled outputs
+def test_wgrad_projection_size():
+    # dW of the 7168 -> 2112 projection over 4096 tokens, every output
     M, N, K = 2112, 7168, 4096
-    print("wgrad 2112x7168x4096 sampled", flush=True)
+    print("wgrad 2112x7168x4096", flush=True)
     a, sa, b, sb = operands(M, N, K, seed=5)
     got = run(a, sa, b, sb)
-    rng = np.random.default_rng(6)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 40)]))
-    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 60)]))
-    ref = gemm.wgrad_f64(a[rows], sa[:, rows], b[cols], sb[:, cols]).astype(np.float32).astype(np.float64)
-    assert_gemm_close(got[np.ix_(rows, cols)], ref, "wgrad sampled")
+    ref = gemm.wgrad_ref(a, sa, b, sb).astype(np.float64)
+    assert_gemm_close(got, ref, "wgrad 2112x7168x4096")
 
 
 def test_wgrad_after_gpu_transpose_chain():
