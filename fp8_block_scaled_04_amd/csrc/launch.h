@@ -44,5 +44,8 @@ struct GemmProblem {
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+// The ping-pong kernel on 192x192 tiles (dense and contiguous layouts; the
+// rows of sA must be a multiple of 4).
+hipError_t launch_gemm_pp192(const GemmProblem& p, hipStream_t stream);
 
 }  // namespace fp8bs

@@ -121,3 +121,17 @@ def test_gemm_decode_shape_pow2_full():
     d = run(a, sa, b, sb)
     ref = bf16.to_f32(gemm.gemm_ref(a, sa, b, sb)).astype(np.float64)
     assert_gemm_close(out_host_f64(d), ref, "gemm 128x24576x1536")
+
+
+@pytest.mark.parametrize("K", [128, 256, 512, 640, 896])
+@pytest.mark.parametrize("M,N", [(4000, 2112), (4096, 2048)])
+def test_gemm_192_tile_chunk_counts(M, N, K):
+    # the 192x192 tile's three-stage pipeline with 1, 2, 4, 5 and 7 chunks
+    # (loop and tail), ragged last row and column tiles, BF16 and FP32 out
+    print(f"gemm 192 tile M={M} N={N} K={K}", flush=True)
+    a, sa, b, sb = operands(M, N, K, seed=M + N + K)
+    ref = gemm.gemm_f64(a, sa, b, sb)
+    d = run(a, sa, b, sb)
+    assert_gemm_close(out_host_f64(d), bf16.to_f32(gemm.round_out(ref, "bf16")).astype(np.float64), f"gemm {M}x{N}x{K}")
+    d = run(a, sa, b, sb, torch.float32)
+    assert_gemm_close(out_host_f64(d), gemm.round_out(ref, "f32").astype(np.float64), f"gemm {M}x{N}x{K} f32")
