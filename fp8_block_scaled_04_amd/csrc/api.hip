@@ -227,6 +227,24 @@ fp8bs_status fp8bs_grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, co
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
 }
 
+fp8bs_status fp8bs_gemm_tile(int32_t layout, int64_t rows, int64_t N, int64_t K, int32_t G, uint32_t flags,
+                             int32_t* tile_m, int32_t* tile_n, int32_t* ping_pong) {
+  if (layout < 0 || layout > 3) return FP8BS_ERR_FLAGS;
+  if (fp8bs_status e = gemm_common(N, K, FP8BS_OUT_BF16)) return e;
+  if (rows < 0 || G < 0) return FP8BS_ERR_SHAPE;
+  if ((layout == 0 || layout == 3) && G != 1) return FP8BS_ERR_SHAPE;
+  if (layout == 1 && rows % 128) return FP8BS_ERR_SHAPE;
+  if (!grid_fits(rows, N, layout == 2 ? G : 1) || !buffers_fit(rows, N, K, layout == 3)) return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
+  if (layout == 3 && flags) return FP8BS_ERR_FLAGS;
+  if (!tile_m || !tile_n || !ping_pong) return FP8BS_ERR_NULL;
+  static const fp8bs::GemmMode modes[4] = {fp8bs::kDense, fp8bs::kContiguous, fp8bs::kMasked, fp8bs::kWgrad};
+  GemmProblem p{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, rows, N, K, G, false, false,
+                (flags & FP8BS_SCALE_POW2) != 0, modes[layout]};
+  fp8bs::gemm_tile(p, *tile_m, *tile_n, *ping_pong);
+  return FP8BS_OK;
+}
+
 fp8bs_status fp8bs_cast_f32_to_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream_t stream) {
   if (n < 0) return FP8BS_ERR_SHAPE;
   if (n == 0) return FP8BS_OK;

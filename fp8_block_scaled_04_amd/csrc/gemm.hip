@@ -731,20 +731,22 @@ double est_rounds(int64_t tiles, double cost) {
   return (double)((per_xcd + slots - 1) / slots) * cost;
 }
 
+// Tile configurations the dispatcher chooses from.
+enum TileChoice { kStream, kSmall, kLarge, kMid, kT192, kPP192, kMaskedT, kWgradMid };
+
 template <int MODE>
-hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
+TileChoice choose(const GemmProblem& p) {
   if constexpr (MODE == kMasked) {
     // Memory-bound decode shapes: the masked tile, once there are enough
     // tiles to fill the GPU.
     const int64_t masked_tiles = ((p.M * p.G + MaskedTile::BM - 1) / MaskedTile::BM) *
                                  ((p.N + MaskedTile::BN - 1) / MaskedTile::BN);
-    if (masked_tiles >= 256) return launch_cfg<MaskedTile, MODE>(p, stream);
-    return launch_cfg<SmallTile, MODE>(p, stream);
+    return masked_tiles >= 256 ? kMaskedT : kSmall;
   } else {
     // Few rows (decode): the weights stream from HBM once; a deep pipeline
     // over many small tiles keeps enough bytes in flight.
     if constexpr (MODE == kDense) {
-      if (p.M <= 128) return launch_cfg<StreamTile, MODE>(p, stream);
+      if (p.M <= 128) return kStream;
     }
     // Row tiles: dense exact; contiguous counts on average half a partial
     // tile per group.
@@ -756,22 +758,66 @@ hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
     const double t_small = est_rounds<SmallTile>(mtiles(128) * ((p.N + 127) / 128), 0.52);
     if constexpr (MODE == kWgrad) {
       // per-row weight scales are read in the 256-wide tiles' loop only
-      if (t_large <= t_mid) return launch_cfg<LargeTile, MODE>(p, stream);
-      return launch_cfg<WgradMidTile, MODE>(p, stream);
+      return t_large <= t_mid ? kLarge : kWgradMid;
     } else {
       const double t_192 = est_rounds<Tile192>(mtiles(192) * ((p.N + 191) / 192), 0.65);
-      if (t_large <= t_mid && t_large <= t_192 && t_large <= t_small) return launch_cfg<LargeTile, MODE>(p, stream);
+      if (t_large <= t_mid && t_large <= t_192 && t_large <= t_small) return kLarge;
       // (on a tie the 128x128 tile: contiguous groups are multiples of 128
       // rows, so their partial 192-row tiles waste more; 8x8192x4096x7168
       // measured 265 us on 128x128 against 273 us on 192x192)
       if (t_192 <= t_mid && t_192 < t_small) {
-        if constexpr (MODE == kDense)
-          if (p.M % 4 == 0) return launch_gemm_pp192(p, stream);
-        return launch_cfg<Tile192, MODE>(p, stream);
+        // the ping-pong loop moves the activation scales 4 rows per lane
+        if (MODE == kDense && p.M % 4 == 0) return kPP192;
+        return kT192;
       }
-      if (t_mid <= t_small) return launch_cfg<MidTile, MODE>(p, stream);
-      return launch_cfg<SmallTile, MODE>(p, stream);
+      return t_mid <= t_small ? kMid : kSmall;
     }
+  }
+}
+
+// The tiles choose() can return for each layout; only those are
+// instantiated.
+constexpr bool possible(int mode, TileChoice c) {
+  switch (mode) {
+    case kDense: return c == kStream || c == kSmall || c == kLarge || c == kMid || c == kT192 || c == kPP192;
+    case kContiguous: return c == kSmall || c == kLarge || c == kMid || c == kT192;
+    case kMasked: return c == kMaskedT || c == kSmall;
+    default: return c == kLarge || c == kWgradMid;
+  }
+}
+
+template <class C, int MODE, TileChoice T>
+hipError_t launch_if(const GemmProblem& p, hipStream_t stream) {
+  if constexpr (possible(MODE, T)) return launch_cfg<C, MODE>(p, stream);
+  else return hipErrorInvalidValue;
+}
+
+template <int MODE>
+hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
+  switch (choose<MODE>(p)) {
+    case kStream: return launch_if<StreamTile, MODE, kStream>(p, stream);
+    case kSmall: return launch_if<SmallTile, MODE, kSmall>(p, stream);
+    case kLarge: return launch_if<LargeTile, MODE, kLarge>(p, stream);
+    case kT192: return launch_if<Tile192, MODE, kT192>(p, stream);
+    case kPP192: return launch_gemm_pp192(p, stream);
+    case kMaskedT: return launch_if<MaskedTile, MODE, kMaskedT>(p, stream);
+    case kWgradMid: return launch_if<WgradMidTile, MODE, kWgradMid>(p, stream);
+    default: return launch_if<MidTile, MODE, kMid>(p, stream);
+  }
+}
+
+template <int MODE>
+void tile_of(const GemmProblem& p, int32_t& bm, int32_t& bn, int32_t& pp) {
+  pp = 0;
+  switch (choose<MODE>(p)) {
+    case kStream: bm = StreamTile::BM; bn = StreamTile::BN; break;
+    case kSmall: bm = SmallTile::BM; bn = SmallTile::BN; break;
+    case kLarge: bm = LargeTile::BM; bn = LargeTile::BN; break;
+    case kT192: bm = Tile192::BM; bn = Tile192::BN; break;
+    case kPP192: bm = 192; bn = 192; pp = 1; break;
+    case kMaskedT: bm = MaskedTile::BM; bn = MaskedTile::BN; break;
+    case kWgradMid: bm = WgradMidTile::BM; bn = WgradMidTile::BN; break;
+    default: bm = MidTile::BM; bn = MidTile::BN; break;
   }
 }
 
@@ -783,6 +829,15 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
     case kContiguous: return dispatch<kContiguous>(p, stream);
     case kWgrad: return dispatch<kWgrad>(p, stream);
     default: return dispatch<kMasked>(p, stream);
+  }
+}
+
+void gemm_tile(const GemmProblem& p, int32_t& bm, int32_t& bn, int32_t& pp) {
+  switch (p.mode) {
+    case kDense: tile_of<kDense>(p, bm, bn, pp); break;
+    case kContiguous: tile_of<kContiguous>(p, bm, bn, pp); break;
+    case kWgrad: tile_of<kWgrad>(p, bm, bn, pp); break;
+    default: tile_of<kMasked>(p, bm, bn, pp); break;
   }
 }
 

@@ -44,6 +44,9 @@ struct GemmProblem {
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+// The tile (rows x columns) launch_gemm uses for p, and whether it runs the
+// ping-pong main loop (host only).
+void gemm_tile(const GemmProblem& p, int32_t& bm, int32_t& bn, int32_t& pp);
 // The ping-pong kernel on 192x192 tiles (dense and contiguous layouts; the
 // rows of sA must be a multiple of 4).
 hipError_t launch_gemm_pp192(const GemmProblem& p, hipStream_t stream);

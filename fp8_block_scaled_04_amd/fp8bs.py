@@ -50,6 +50,7 @@ _gmask = _sig("fp8bs_grouped_gemm_fp8_masked",
 _cast = _sig("fp8bs_cast_f32_to_e4m3", [_P, _I64, _P, _P])
 _t128 = _sig("fp8bs_transpose_128x128", [_P, _P, _I64, _I64, _I64, _P, _P, _P])
 _qdual = _sig("fp8bs_quantize_dual", [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P])
+_gtile = _sig("fp8bs_gemm_tile", [_I32, _I64, _I64, _I64, _I32, _U32, _P, _P, _P])
 _lib.fp8bs_status_str.argtypes = [ctypes.c_int]
 _lib.fp8bs_status_str.restype = ctypes.c_char_p
 _lib.fp8bs_abi_version.argtypes = []
@@ -311,3 +312,17 @@ def cast_to_e4m3(x: torch.Tensor) -> torch.Tensor:
     q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
     _check(_cast(_ptr(x), x.numel(), _ptr(q), _stream(x)), "cast_f32_to_e4m3")
     return q
+
+
+GEMM_LAYOUTS = {"dense": 0, "contiguous": 1, "masked": 2, "wgrad": 3}
+
+
+def gemm_tile(layout: str, rows: int, N: int, K: int, G: int = 1, pow2_scales: bool = False):
+    """(tile_m, tile_n, ping_pong) the GEMM call of `layout` ("dense",
+    "contiguous", "masked", "wgrad") would run on; host-side, no device work.
+    rows is M, Mt or cap."""
+    out = (ctypes.c_int32 * 3)()
+    base = ctypes.addressof(out)
+    _check(_gtile(GEMM_LAYOUTS[layout], rows, N, K, G, SCALE_POW2 if pow2_scales else 0,
+                  base, base + 4, base + 8), "gemm_tile")
+    return int(out[0]), int(out[1]), int(out[2])

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 2
+#define FP8BS_ABI_VERSION 3
 
 /* Same type as hipStream_t; declared here so the header needs no HIP headers. */
 struct ihipStream_t;
@@ -271,6 +271,25 @@ fp8bs_status fp8bs_grouped_gemm_fp8_masked(const uint8_t* a, const float* sa,
  */
 fp8bs_status fp8bs_cast_f32_to_e4m3(const float* x, int64_t n, uint8_t* q,
                                     fp8bs_stream_t stream);
+
+/*
+ * Tile a GEMM call would run on (host-side query: no device, no launch; for
+ * tests and tuning, not part of the method the pages describe).
+ *   layout : 0 dense (fp8bs_gemm_fp8_blockscaled), 1 contiguous grouped,
+ *            2 masked grouped, 3 weight gradient
+ *   rows   : M (dense, weight gradient), Mt (contiguous) or cap (masked)
+ *   N, K, G, flags : as passed to that call (G = 1 for dense and weight
+ *            gradient)
+ *   tile_m, tile_n : HOST pointers, receive the output tile (rows x columns
+ *            per workgroup)
+ *   ping_pong : HOST pointer, receives 1 if the tile runs the ping-pong main
+ *            loop (two wave groups alternating fragment loads and MFMAs),
+ *            0 otherwise
+ * The size and flag checks of the named call apply (same status codes);
+ * null output pointers give FP8BS_ERR_NULL.
+ */
+fp8bs_status fp8bs_gemm_tile(int32_t layout, int64_t rows, int64_t N, int64_t K, int32_t G,
+                             uint32_t flags, int32_t* tile_m, int32_t* tile_n, int32_t* ping_pong);
 
 /* Static, NUL-terminated description of a status code (host memory). */
 const char* fp8bs_status_str(fp8bs_status status);

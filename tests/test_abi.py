@@ -46,7 +46,7 @@ def lib(lib_path):
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in fp8bs.h but not exported"
 
@@ -171,7 +171,7 @@ def test_cast_validation(lib):
 def test_binding_imports_and_reports_its_library(lib_path):
     from fp8_block_scaled_04_amd import fp8bs
     assert fp8bs.library() == lib_path
-    assert fp8bs.abi_version() == 2
+    assert fp8bs.abi_version() == 3
 
 
 def test_package_exports_every_binding_function(lib_path):
@@ -247,3 +247,50 @@ def test_gemm_rejects_sizes_beyond_32bit_addressing(lib):
     # inside the limits: the arguments pass and the device check answers
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 17, 256, 1 << 17, 0, 0, None) == DEVICE   # 4*(K/128)*M = 2^29
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 2112, 7168, 0, 0, None) == DEVICE
+
+
+def test_gemm_tile_query_validation(lib):
+    f = fn(lib, "fp8bs_gemm_tile", [I32, I64, I64, I64, I32, U32, P, P, P])
+    out = (ctypes.c_int32 * 3)()
+    o = ctypes.addressof(out)
+    assert f(4, 128, 256, 512, 1, 0, o, o + 4, o + 8) == FLAGS          # unknown layout
+    assert f(0, 128, 24, 512, 1, 0, o, o + 4, o + 8) == SHAPE           # N % 16
+    assert f(0, 128, 256, 500, 1, 0, o, o + 4, o + 8) == SHAPE          # K % 128
+    assert f(0, 128, 256, 512, 2, 0, o, o + 4, o + 8) == SHAPE          # dense takes G = 1
+    assert f(1, 100, 256, 512, 2, 0, o, o + 4, o + 8) == SHAPE          # Mt % 128
+    assert f(0, 128, 256, 512, 1, 2, o, o + 4, o + 8) == FLAGS
+    assert f(3, 128, 256, 512, 1, 1, o, o + 4, o + 8) == FLAGS          # no pow2 weight gradient
+    assert f(0, 128, 256, 512, 1, 0, None, o + 4, o + 8) == NULL
+    assert f(0, 128, 256, 512, 1, 0, o, o + 4, o + 8) == OK and tuple(out) == (128, 96, 0)
+
+
+# The tile each benchmark workload and each labelled parity case runs on
+# (host-side dispatch, no GPU): the parity tests' labels cannot drift from
+# what the dispatcher does.
+TILES = [
+    (("dense", 4096, 2112, 7168), (192, 192, 1)),        # training projection: ping-pong loop
+    (("dense", 4001, 2112, 7168), (192, 192, 0)),        # rows not a multiple of 4: the other loop
+    (("dense", 8192, 4096, 7168), (256, 256, 0)),
+    (("dense", 128, 24576, 1536), (128, 96, 0)),         # decode
+    (("dense", 4096, 7168, 2176), (256, 256, 0)),        # data gradient
+    (("dense", 4000, 7168, 256), (256, 256, 0)),         # ragged rows on 256x256
+    (("dense", 4096, 4096, 256), (256, 256, 0)),
+    (("dense", 4000, 4112, 384), (192, 192, 1)),
+    (("dense", 2304, 4096, 256), (256, 160, 0)),
+    (("dense", 2560, 3584, 384), (256, 160, 0)),
+    (("dense", 2450, 3696, 256, 1, True), (256, 160, 0)),     # power-of-two scales
+    (("dense", 4096, 2112, 1024, 1, True), (192, 192, 1)),
+    (("contiguous", 8192, 4096, 7168, 8), (128, 128, 0)),
+    (("contiguous", 1408, 7168, 256, 3), (256, 256, 0)),
+    (("contiguous", 1152, 7168, 256, 2), (256, 160, 0)),
+    (("contiguous", 2048, 4096, 256, 2), (192, 192, 0)),
+    (("masked", 256, 7168, 2048, 32), (128, 256, 0)),
+    (("wgrad", 2112, 7168, 4096), (256, 256, 0)),
+    (("wgrad", 300, 208, 384), (256, 160, 0)),
+]
+
+
+@pytest.mark.parametrize("args,tile", TILES)
+def test_gemm_tile_choice(lib_path, args, tile):
+    from fp8_block_scaled_04_amd import fp8bs
+    assert fp8bs.gemm_tile(*args) == tile

@@ -14,8 +14,8 @@ import torch
 
 from fp8_block_scaled_04_amd import fp8bs, synth
 from oracle import bf16, e4m3, gemm, quantize
-from tests.gpu_util import (assert_codes_equal, assert_gemm_close, codes_dev, f32_dev, i32_dev, out_host_f64,
-                            require_gpu)
+from tests.gpu_util import (assert_codes_equal, assert_gemm_close, codes_dev, contiguous_allowance, dense_allowance,
+                            f32_dev, i32_dev, masked_allowance, out_host_f64, require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def ref_out(a, sa, b, sb, out_dtype):
 
 # shapes that reach every tile: 128x128 (double-buffered), 192x192 (4096x2112,
 # 4000x4112), 256x160 (2450x3696), 256x256, 128x96 (few rows), with ragged edges
-@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (37, 48, 384), (300, 400, 640), (4096, 2112, 1024),
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (37, 48, 384), (300, 400, 640), (4096, 2112, 1024), (4000, 7168, 256),
                                    (4096, 4096, 256), (4000, 4112, 384), (2450, 3696, 256), (128, 24576, 1536),
                                    (1, 16, 128)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
@@ -53,7 +53,8 @@ def test_pow2_recipe(M, N, K, out_dtype):
     print(f"pow2 gemm M={M} N={N} K={K} out={out_dtype}", flush=True)
     a, sa, b, sb = operands(M, N, K, seed=M + 5 * N + K)
     d = run(a, sa, b, sb, out_dtype)
-    assert_gemm_close(out_host_f64(d), ref_out(a, sa, b, sb, out_dtype), f"pow2 gemm {M}x{N}x{K}")
+    assert_gemm_close(out_host_f64(d), ref_out(a, sa, b, sb, out_dtype), f"pow2 gemm {M}x{N}x{K}",
+                      dense_allowance(a, sa, b, sb))
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 272, 1024), (4000, 4112, 256), (4096, 2112, 512), (4096, 4096, 256)])
@@ -109,19 +110,37 @@ def test_pow2_invalid_scale_gives_nan_only_where_used():
     assert_gemm_close(got[~bad], good_ref[~bad], "pow2 outputs with valid scales")
 
 
-def test_pow2_contiguous():
-    G, Mt, N, K = 4, 1152, 2112, 384
-    w = synth.contiguous(G, Mt, N, K, seed=9)
+@pytest.mark.parametrize("G,Mt,N,K,offsets,tile", [
+    (4, 1152, 2112, 384, [0, 128, 128, 640, 1024], (128, 128)),
+    # 256x256 and 256x160 tiles: groups end half way into 256-row tiles,
+    # rows past the last group must stay untouched
+    (3, 1408, 7168, 256, [0, 384, 384, 1152], (256, 256)),
+    (2, 1152, 7168, 256, [0, 640, 1024], (256, 160)),
+])
+def test_pow2_contiguous(G, Mt, N, K, offsets, tile):
+    assert fp8bs.gemm_tile("contiguous", Mt, N, K, G, pow2_scales=True)[:2] == tile
+    print(f"pow2 contiguous G={G} Mt={Mt} N={N} K={K} tile {tile}", flush=True)
+    w = synth.contiguous(G, Mt, N, K, seed=9 + G)
     a, sa = quantize.quantize_1x128(w["a"], pow2=True)
     b, sb = quantize.quantize_128x128(w["b"], pow2=True)
-    offs = np.array([0, 128, 128, 640, 1024], np.int32)
+    offs = np.array(offsets, np.int32)
+    ref = gemm.grouped_contiguous_f64(a, sa, b, sb, offs)
+    used = ~np.isnan(ref[:, 0])
     d = fp8bs.grouped_gemm_contiguous(codes_dev(a), f32_dev(sa), codes_dev(b), f32_dev(sb), i32_dev(offs),
                                       out_dtype=torch.float32, pow2_scales=True)
     torch.cuda.synchronize()
-    ref = gemm.grouped_contiguous_f64(a, sa, b, sb, offs)
-    used = ~np.isnan(ref[:, 0])
+    allow = contiguous_allowance(a, sa, b, sb, offs, np.nonzero(used)[0])
     assert_gemm_close(d.cpu().numpy().astype(np.float64)[used], ref[used].astype(np.float32).astype(np.float64),
-                      "pow2 contiguous")
+                      "pow2 contiguous fp32", allow)
+    sentinel = 0x7FC1
+    out = torch.full((Mt, N), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    fp8bs.grouped_gemm_contiguous(codes_dev(a), f32_dev(sa), codes_dev(b), f32_dev(sb), i32_dev(offs), out=out,
+                                  pow2_scales=True)
+    torch.cuda.synchronize()
+    raw = out.view(torch.int16).cpu().numpy()
+    assert (raw[~used] == sentinel).all(), "rows outside every group were written"
+    ref_b = bf16.to_f32(bf16.from_f64_rne(ref[used])).astype(np.float64)
+    assert_gemm_close(out.float().cpu().numpy().astype(np.float64)[used], ref_b, "pow2 contiguous bf16", allow)
 
 
 @pytest.mark.parametrize("G,cap,N,K,counts", [(3, 256, 96, 256, [0, 256, 77]),
@@ -146,4 +165,5 @@ def test_pow2_masked(G, cap, N, K, counts):
     valid = ~np.isnan(ref[:, :, 0])
     got = out.cpu().numpy().astype(np.float64)
     assert np.isnan(got[~valid]).all(), "rows past the count were written"
-    assert_gemm_close(got[valid], ref[valid].astype(np.float32).astype(np.float64), "pow2 masked")
+    assert_gemm_close(got[valid], ref[valid].astype(np.float32).astype(np.float64), "pow2 masked",
+                      masked_allowance(a, sa, b, sb, valid))

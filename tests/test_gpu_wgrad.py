@@ -14,7 +14,7 @@ import torch
 
 from fp8_block_scaled_04_amd import fp8bs, synth
 from oracle import e4m3, gemm, quantize
-from tests.gpu_util import assert_gemm_close, bf16_dev, codes_dev, codes_host, f32_dev, require_gpu
+from tests.gpu_util import assert_gemm_close, bf16_dev, codes_dev, codes_host, dense_allowance, f32_dev, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,7 @@ def test_wgrad_recipe(M, N, K, accumulate):
     d_in = np.random.default_rng(M + N).standard_normal((M, N)).astype(np.float32) if accumulate else None
     got = run(a, sa, b, sb, d_in)
     ref = gemm.wgrad_ref(a, sa, b, sb, d_in).astype(np.float64)
-    assert_gemm_close(got, ref, f"wgrad {M}x{N}x{K}")
+    assert_gemm_close(got, ref, f"wgrad {M}x{N}x{K}", dense_allowance(a, sa, b, sb, wgrad=True))
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 320, 1024), (2000, 7008, 384)])
@@ -76,7 +76,7 @@ def test_wgrad_projection_size():
     a, sa, b, sb = operands(M, N, K, seed=5)
     got = run(a, sa, b, sb)
     ref = gemm.wgrad_ref(a, sa, b, sb).astype(np.float64)
-    assert_gemm_close(got, ref, "wgrad 2112x7168x4096")
+    assert_gemm_close(got, ref, "wgrad 2112x7168x4096", dense_allowance(a, sa, b, sb, wgrad=True))
 
 
 def test_wgrad_after_gpu_transpose_chain():
