@@ -112,6 +112,20 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_pp(const GemmArgs p) {
   // operand-row DMAs, and for wave 0 (SCW) the activation-scale DMA.  Chunks
   // past the end use a zero-record descriptor: zeros land in LDS and no
   // memory is read.
+  // DMA instruction i of that share (i == LOADS: the scale DMA, wave 0 only).
+  auto issue_one = [&](int kb, int stage, int i, auto scw) __attribute__((always_inline)) {
+    const uint32_t st = smem_lds + stage * C::STAGE;
+    const bool live = kb < KT;
+    if (i < C::LOADS) {
+      const uint32_t koff = live ? (uint32_t)kb * kKC : 0u;
+      uint32_t ro = row_off;
+      asm volatile("" : "+v"(ro));
+      dma16(live ? rop : r_none, st + op_lds + (4 * i + s) * 8 * kKC, ro + i * row_step, koff);
+    } else if constexpr (decltype(scw)::value) {
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(live ? (uint32_t)kb * sa_step : 0u);
+      dma16(live ? rsa : r_none, st + C::SA_OFF, sa_voff, soff);
+    }
+  };
   auto issue = [&](int kb, int stage, auto scw) __attribute__((always_inline)) {
     const uint32_t st = smem_lds + stage * C::STAGE;
     const bool live = kb < KT;
@@ -166,13 +180,14 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_pp(const GemmArgs p) {
   };
 
   // Load phase of chunk kb (in stage `stage`): read this wave's scales and
-  // fragments, then start this wave's share of chunk kb+2's DMA into the
-  // stage chunk kb-1 used (its issue waits for the texture unit, which the
-  // LDS reads already in flight do not), then form the scale products.  The
-  // DMA is issued here, not between the MFMAs: a DMA waiting for the
-  // texture unit would hold up the MFMA stream behind it (measured on
-  // 4096x2112x7168: 63.4 us here, 65.9 us with half of each wave's share
-  // spread through its compute phase).
+  // fragments, with this wave's share of chunk kb+2's DMA (into the stage
+  // chunk kb-1 used) interleaved, one DMA after every two fragments, so the
+  // LDS and the texture unit work at the same time; then form the scale
+  // products.  The DMA is issued here, not between the MFMAs: a DMA waiting
+  // for the texture unit would hold up the MFMA stream behind it (measured
+  // on 4096x2112x7168: 63.4 us with the DMA after the reads, 65.9 us with
+  // half of each wave's share spread through its compute phase, 59.9 us
+  // interleaved with the reads, that one with the epilogue below).
   auto load = [&](int kb, int stage, auto scw) __attribute__((always_inline)) {
     const uint8_t* st = smem + stage * C::STAGE;
     float sa[FM];
@@ -180,13 +195,29 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_pp(const GemmArgs p) {
     for (int j = 0; j < FM; ++j) sa[j] = reinterpret_cast<const float*>(st + C::SA_OFF)[a_row0 + 16 * j + fr];
     const float sb_lo = sbc[sb_lo_off + kb];
     const float sb_hi = sbc[sb_hi_off + kb];   // used only by fragments past the block boundary
+    {
+      const int dst_stage = stage == 0 ? 2 : stage - 1;
+      // fragment f (0 .. FM+FN-1), and DMA instruction d after every
+      // EVERY fragments; the rest after the last fragment
+      constexpr int NF = FM + FN;
+      constexpr int NDMA = C::LOADS + 1;
+      constexpr int EVERY = (NF + NDMA - 1) / NDMA;
+      int d = 0;
 #pragma unroll
-    for (int j = 0; j < FM; ++j) fa[j] = read_frag(st + (a_row0 + 16 * j) * kKC);
+      for (int f = 0; f < NF; ++f) {
+        if (f < FM) fa[f] = read_frag(st + (a_row0 + 16 * f) * kKC);
+        else fb[f - FM] = read_frag(st + C::A_BYTES + (b_row0 + 16 * (f - FM)) * kKC);
+        if ((f + 1) % EVERY == 0 && d < NDMA) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_one(kb + 2, dst_stage, d, scw);
+          __builtin_amdgcn_sched_barrier(0);
+          ++d;
+        }
+      }
 #pragma unroll
-    for (int i = 0; i < FN; ++i) fb[i] = read_frag(st + C::A_BYTES + (b_row0 + 16 * i) * kKC);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(kb + 2, stage == 0 ? 2 : stage - 1, scw);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int dd = (NF / EVERY); dd < NDMA; ++dd) issue_one(kb + 2, dst_stage, dd, scw);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (HWS) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) ea[j] = e8m0_of(sa[j]);
@@ -285,24 +316,40 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_pp(const GemmArgs p) {
   }
   __builtin_amdgcn_s_waitcnt(0);   // no LDS write may still be in flight at exit
 
-  // ---- epilogue: lane holds D[m][n .. n+3] per fragment ------------------
+  // ---- epilogue: through LDS, then whole rows -----------------------------
+  // Every tile stores at the same moment, so the epilogue is a burst of the
+  // whole output; written from the fragments directly (8 bytes per lane, 32
+  // bytes per row segment) it took 2.2 us longer on 4096x2112x384 than
+  // staged in the free LDS and stored in 16-byte pieces of whole rows.
   const int64_t m_valid = t.m_valid, d_row0 = t.d_row0;
+  constexpr int ES = OUT_F32 ? 4 : 2;                 // bytes per output
+  constexpr int RSTR = BN * ES + 16;                  // LDS row stride (padded)
+  static_assert(BM * RSTR <= C::LDS_BYTES, "the output tile fits in LDS");
+  __builtin_amdgcn_s_barrier();                       // every wave is done with the stages
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
-    const int64_t n = n0 + b_row0 + 16 * i + 4 * fg;
+    const int col = b_row0 + 16 * i + 4 * fg;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int64_t m = m0 + a_row0 + 16 * j + fr;
-      if (m < m_valid && n < N) {
-        const int64_t idx = (d_row0 + m) * N + n;
-        if (OUT_F32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.d) + idx) =
-              make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        } else {
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.d) + idx) =
-              make_uint2(pack2_bf16(acc[i][j][0], acc[i][j][1]), pack2_bf16(acc[i][j][2], acc[i][j][3]));
-        }
+      const int row = a_row0 + 16 * j + fr;
+      uint8_t* dst = smem + row * RSTR + col * ES;
+      if (OUT_F32) {
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      } else {
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2(pack2_bf16(acc[i][j][0], acc[i][j][1]), pack2_bf16(acc[i][j][2], acc[i][j][3]));
       }
+    }
+  }
+  __builtin_amdgcn_s_barrier();
+  constexpr int CPR = BN * ES / 16;                   // 16-byte pieces per row
+  const int64_t rows = min<int64_t>(m_valid - m0, BM);
+  const int64_t cols = min<int64_t>(N - n0, BN);      // a multiple of 8 (N % 16 == 0)
+  for (int q = threadIdx.x; q < BM * CPR; q += C::THREADS) {
+    const int row = q / CPR, piece = q - row * CPR;
+    if (row < rows && piece * 16 < cols * ES) {
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + row * RSTR + piece * 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(p.d) + ((d_row0 + m0 + row) * N + n0) * ES + piece * 16) = v;
     }
   }
 #endif
