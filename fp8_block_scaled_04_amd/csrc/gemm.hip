@@ -760,16 +760,16 @@ TileChoice choose(const GemmProblem& p) {
       // per-row weight scales are read in the 256-wide tiles' loop only
       return t_large <= t_mid ? kLarge : kWgradMid;
     } else {
-      const double t_192 = est_rounds<Tile192>(mtiles(192) * ((p.N + 191) / 192), 0.65);
+      // The 192x192 tile runs the ping-pong loop (gemm_pp.hip) whenever the
+      // rows of sA are a multiple of 4 (it moves them 4 rows per lane; always
+      // so for the contiguous layout, whose rows are a multiple of 128): it
+      // costs 0.56 of a 256x256 tile (4096x2112x7168 in 60 against about 70
+      // us for the 0.65 of the 12-wave 192x192 tile).  On 8x8192x4096x7168
+      // contiguous it took 269 us against 289 us on 128x128 tiles.
+      const bool pp = MODE == kContiguous || p.M % 4 == 0;
+      const double t_192 = est_rounds<Tile192>(mtiles(192) * ((p.N + 191) / 192), pp ? 0.56 : 0.65);
       if (t_large <= t_mid && t_large <= t_192 && t_large <= t_small) return kLarge;
-      // (on a tie the 128x128 tile: contiguous groups are multiples of 128
-      // rows, so their partial 192-row tiles waste more; 8x8192x4096x7168
-      // measured 265 us on 128x128 against 273 us on 192x192)
-      if (t_192 <= t_mid && t_192 < t_small) {
-        // the ping-pong loop moves the activation scales 4 rows per lane
-        if (MODE == kDense && p.M % 4 == 0) return kPP192;
-        return kT192;
-      }
+      if (t_192 <= t_mid && t_192 < t_small) return pp ? kPP192 : kT192;
       return t_mid <= t_small ? kMid : kSmall;
     }
   }
@@ -780,7 +780,7 @@ TileChoice choose(const GemmProblem& p) {
 constexpr bool possible(int mode, TileChoice c) {
   switch (mode) {
     case kDense: return c == kStream || c == kSmall || c == kLarge || c == kMid || c == kT192 || c == kPP192;
-    case kContiguous: return c == kSmall || c == kLarge || c == kMid || c == kT192;
+    case kContiguous: return c == kSmall || c == kLarge || c == kMid || c == kPP192;
     case kMasked: return c == kMaskedT || c == kSmall;
     default: return c == kLarge || c == kWgradMid;
   }

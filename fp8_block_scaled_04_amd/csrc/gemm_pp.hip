@@ -263,6 +263,10 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_pp(const GemmArgs p) {
           const int pb = b - 2;
           fma_block(acc[pb / FM][pb % FM], pc[(base + pb) % 3], sc[pb / FM][pb % FM]);
         }
+        // the MFMA first: its FMAs then read a partial two MFMAs old (no
+        // hazard waits), and the MFMA issues as soon as the matrix core is free
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -280,10 +280,11 @@ TILES = [
     (("dense", 2560, 3584, 384), (256, 160, 0)),
     (("dense", 2450, 3696, 256, 1, True), (256, 160, 0)),     # power-of-two scales
     (("dense", 4096, 2112, 1024, 1, True), (192, 192, 1)),
-    (("contiguous", 8192, 4096, 7168, 8), (128, 128, 0)),
+    (("contiguous", 8192, 4096, 7168, 8), (192, 192, 1)),   # MoE workload: ping-pong loop
     (("contiguous", 1408, 7168, 256, 3), (256, 256, 0)),
     (("contiguous", 1152, 7168, 256, 2), (256, 160, 0)),
-    (("contiguous", 2048, 4096, 256, 2), (192, 192, 0)),
+    (("contiguous", 2048, 4096, 256, 2), (192, 192, 1)),
+    (("contiguous", 4608, 4096, 256, 7), (128, 128, 0)),
     (("masked", 256, 7168, 2048, 32), (128, 256, 0)),
     (("wgrad", 2112, 7168, 4096), (256, 256, 0)),
     (("wgrad", 300, 208, 384), (256, 160, 0)),

@@ -50,8 +50,8 @@ def run_contiguous(a, sa, b, sb, offs, Mt, N):
     (2, 256, 16, 384, [0, 0, 0]),                    # every group empty
     # 128x128 tiles at size: 128-row groups, one group is empty
     (7, 4608, 4096, 256, [0, 128, 128, 1152, 2304, 2432, 3840, 4480]),
-    # the 192x192 tile: groups of 640 and 1280 rows end inside a tile, rows
-    # 1920.. unused
+    # the 192x192 tile (ping-pong loop): groups of 640 and 1280 rows end
+    # inside a tile, rows 1920.. unused
     (2, 2048, 4096, 256, [0, 640, 1920]),
     # the 256x256 tile: a group of 384 rows ends half way into a tile, an
     # empty group, rows 1152.. unused

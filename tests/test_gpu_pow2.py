@@ -116,6 +116,8 @@ def test_pow2_invalid_scale_gives_nan_only_where_used():
     # rows past the last group must stay untouched
     (3, 1408, 7168, 256, [0, 384, 384, 1152], (256, 256)),
     (2, 1152, 7168, 256, [0, 640, 1024], (256, 160)),
+    # the ping-pong 192x192 tile: groups of 640 and 1280 rows end inside tiles
+    (2, 2048, 4096, 256, [0, 640, 1920], (192, 192)),
 ])
 def test_pow2_contiguous(G, Mt, N, K, offsets, tile):
     assert fp8bs.gemm_tile("contiguous", Mt, N, K, G, pow2_scales=True)[:2] == tile
