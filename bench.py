@@ -39,8 +39,9 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 WORKLOAD = dict(name="dense_4096x2112x7168", M=4096, N=2112, K=7168)
 # rocprofv3 summary of the dominant kernel on this workload, and the sources it was built from
 GEMM_PROFILE = "profiles/k_gemm_dense_4096x2112x7168.md"
-GEMM_SOURCES = ["fp8_block_scaled_04_amd/csrc/gemm.hip", "fp8_block_scaled_04_amd/csrc/device_common.h",
-                "fp8_block_scaled_04_amd/csrc/launch.h"]
+GEMM_SOURCES = ["fp8_block_scaled_04_amd/csrc/gemm_pp.hip", "fp8_block_scaled_04_amd/csrc/gemm_common.h",
+                "fp8_block_scaled_04_amd/csrc/device_common.h", "fp8_block_scaled_04_amd/csrc/launch.h"]
+GEMM_KERNEL = "k_gemm_pp (dense, ping-pong 192x192 tile)"
 
 
 def dev_bf16(bits):
@@ -129,10 +130,26 @@ def extra_kernels(fb, synth):
     byt = 2 * M * K + 2 * M * K + 8 * (M * K // 128)
     out["quantize_dual_8192x7168"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
                                           frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
-    # References for the 1:1 read:write stream of the transpose-requantizer:
-    # the code-only 128x128 block transpose of the same 8192 x 7168 codes
-    # (same access pattern, no arithmetic) and a plain device copy of the
-    # same number of bytes.
+    # Practical ceilings on this device: the library's streaming reference
+    # (nontemporal 16-byte loads and stores, no arithmetic) writing the same
+    # M*K bytes while reading twice as many (the 1x128 quantizer's mix) or as
+    # many (the transpose-requantizer's).  Each quantizer's line carries its
+    # fraction of the matching stream's rate.
+    srcs = [torch.empty(2 * M * K, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    dsts = [torch.empty(M * K, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    for ratio in (2, 1):
+        it = iter(range(10 ** 9))
+        us, how = time_graph(lambda: (lambda i: fb.stream_reference(srcs[i % R][:ratio * M * K], dsts[i % R]))(next(it)))
+        byt = (ratio + 1) * M * K
+        out[f"reference_stream_{ratio}to1_{M * K / 1e6:.1f}MB_written"] = dict(
+            us=us, timing=how, GBs=byt / us / 1e3, frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
+    del srcs, dsts
+    for name, ref in (("quantize_1x128_8192x7168", "2to1"), ("quantize_transpose_128x1_8192x7168", "1to1"),
+                      ("quantize_dual_8192x7168", "1to1")):
+        r = out[f"reference_stream_{ref}_{M * K / 1e6:.1f}MB_written"]
+        out[name]["frac_of_stream_reference"] = out[name]["GBs"] / r["GBs"]
+    # The code-only 128x128 block transpose of the same 8192 x 7168 codes
+    # (the transpose-requantizer's access pattern, no arithmetic).
     sw = [torch.ones((1, M // 128, K // 128), device="cuda") for _ in range(R)]
     it = iter(range(10 ** 9))
 
@@ -142,13 +159,7 @@ def extra_kernels(fb, synth):
     byt = 2 * M * K
     out["reference_code_transpose_8192x7168"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
                                                      frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
-    srcs = [torch.empty(M * K, dtype=torch.uint8, device="cuda") for _ in range(R)]
-    dsts = [torch.empty(M * K, dtype=torch.uint8, device="cuda") for _ in range(R)]
-    it = iter(range(10 ** 9))
-    us, how = time_graph(lambda: (lambda i: dsts[i % R].copy_(srcs[i % R]))(next(it)))
-    out["reference_device_copy_58.7MB"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
-                                               frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
-    del xs, qs, x0, sw, srcs, dsts
+    del xs, qs, x0, sw
     torch.cuda.empty_cache()
 
     # decode-shaped GEMM 128 x 24576 x 1536 (power-of-two scales) + its quantizer
@@ -252,9 +263,11 @@ def extra_kernels(fb, synth):
     del qt, st, a, sa
     dw = torch.empty((ayt.shape[0], NI), dtype=torch.float32, device="cuda")
     us, how = time_graph(lambda: fb.gemm_wgrad(ayt, sayt, axt, saxt, out=dw))
-    Mw = ayt.shape[0]
-    out["gemm_wgrad_2176x7168x4096"] = dict(us=us, timing=how, TFLOPs=2 * Mw * NI * T / us / 1e6,
-                                            frac_mfma=2 * Mw * NI * T / us / 1e6 / FP8_PEAK_TFLOPS)
+    # flops on the 2112 valid output rows; the kernel also runs the 64 zero
+    # rows that pad dY^T to whole 128-row blocks
+    out["gemm_wgrad_2112x7168x4096"] = dict(us=us, timing=how, TFLOPs=2 * NO * NI * T / us / 1e6,
+                                            frac_mfma=2 * NO * NI * T / us / 1e6 / FP8_PEAK_TFLOPS,
+                                            rows_run=int(ayt.shape[0]))
     return out
 
 
@@ -564,7 +577,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP8_PEAK_TFLOPS,
                      "traffic": profile_traffic(GEMM_PROFILE, GEMM_SOURCES),
-                     "kernel": "k_gemm (dense)", "kernel_us": gemm_us,
+                     "kernel": GEMM_KERNEL, "kernel_us": gemm_us,
                      "kernel_us_method": kernel_us_method,
                      "kernel_us_burst": gemm_us_burst, "quantizer_us_in_step": quant_us},
     }

@@ -17,7 +17,7 @@ Sub-modules: ``fp8bs`` (the binding, loaded on first use of a public name),
 _PUBLIC = (
     "quantize_1x128", "quantize_transpose_128x1", "quantize_128x128", "quantize_dual",
     "transpose_128x128", "gemm", "gemm_wgrad", "grouped_gemm_contiguous", "grouped_gemm_masked",
-    "cast_to_e4m3", "gemm_tile", "abi_version", "Fp8bsError", "library",
+    "cast_to_e4m3", "gemm_tile", "stream_reference", "abi_version", "Fp8bsError", "library",
 )
 
 __all__ = list(_PUBLIC)

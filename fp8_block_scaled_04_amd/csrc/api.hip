@@ -245,6 +245,19 @@ fp8bs_status fp8bs_gemm_tile(int32_t layout, int64_t rows, int64_t N, int64_t K,
   return FP8BS_OK;
 }
 
+fp8bs_status fp8bs_stream_reference(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
+                                    fp8bs_stream_t stream) {
+  if (dst_bytes < 0 || dst_bytes % 16 || (src_bytes != dst_bytes && src_bytes != 2 * dst_bytes))
+    return FP8BS_ERR_SHAPE;
+  if (dst_bytes == 0) return FP8BS_OK;
+  if (!src || !dst) return FP8BS_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return FP8BS_ERR_ALIGN;
+  if (fp8bs_status e = check_device()) return e;
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_stream_reference(src, dst, dst_bytes, (int)(src_bytes / dst_bytes),
+                                                 (hipStream_t)stream));
+}
+
 fp8bs_status fp8bs_cast_f32_to_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream_t stream) {
   if (n < 0) return FP8BS_ERR_SHAPE;
   if (n == 0) return FP8BS_OK;

@@ -22,6 +22,8 @@ hipError_t launch_quantize_dual(const void* x, int64_t M, int64_t K, uint8_t* q,
 hipError_t launch_transpose_128x128(const uint8_t* q, const float* s, int64_t G, int64_t N, int64_t K, uint8_t* qt,
                                    float* st, hipStream_t stream);
 hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream);
+// Bandwidth reference: dst_bytes written, ratio (1 or 2) times as many read.
+hipError_t launch_stream_reference(const void* src, void* dst, int64_t dst_bytes, int ratio, hipStream_t stream);
 
 // kWgrad: dense layout, but B carries one scale per row per 128 K ([K/128][N],
 // like A) and D is FP32, optionally accumulated into.

@@ -51,6 +51,7 @@ _cast = _sig("fp8bs_cast_f32_to_e4m3", [_P, _I64, _P, _P])
 _t128 = _sig("fp8bs_transpose_128x128", [_P, _P, _I64, _I64, _I64, _P, _P, _P])
 _qdual = _sig("fp8bs_quantize_dual", [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P])
 _gtile = _sig("fp8bs_gemm_tile", [_I32, _I64, _I64, _I64, _I32, _U32, _P, _P, _P])
+_sref = _sig("fp8bs_stream_reference", [_P, _I64, _P, _I64, _P])
 _lib.fp8bs_status_str.argtypes = [ctypes.c_int]
 _lib.fp8bs_status_str.restype = ctypes.c_char_p
 _lib.fp8bs_abi_version.argtypes = []
@@ -326,3 +327,16 @@ def gemm_tile(layout: str, rows: int, N: int, K: int, G: int = 1, pow2_scales: b
     _check(_gtile(GEMM_LAYOUTS[layout], rows, N, K, G, SCALE_POW2 if pow2_scales else 0,
                   base, base + 4, base + 8), "gemm_tile")
     return int(out[0]), int(out[1]), int(out[2])
+
+
+def stream_reference(src: torch.Tensor, dst: torch.Tensor):
+    """Bandwidth reference (not part of the method): stream src into dst with
+    nontemporal loads and stores; src holds as many bytes as dst (a copy) or
+    twice as many (2:1 read:write)."""
+    for t, nm in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous device tensor")
+    nb_s = src.numel() * src.element_size()
+    nb_d = dst.numel() * dst.element_size()
+    _check(_sref(_ptr(src), nb_s, _ptr(dst), nb_d, _stream(src)), "stream_reference")
+    return dst

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 3
+#define FP8BS_ABI_VERSION 4
 
 /* Same type as hipStream_t; declared here so the header needs no HIP headers. */
 struct ihipStream_t;
@@ -270,6 +270,19 @@ fp8bs_status fp8bs_grouped_gemm_fp8_masked(const uint8_t* a, const float* sa,
  *   x : FP32 [n] (input),  q : E4M3 [n] (output).  Requires n >= 0.
  */
 fp8bs_status fp8bs_cast_f32_to_e4m3(const float* x, int64_t n, uint8_t* q,
+                                    fp8bs_stream_t stream);
+
+/*
+ * Bandwidth reference (not a step of the method): streams src to dst with
+ * nontemporal 16-byte loads and stores, reading src_bytes and writing
+ * dst_bytes, where src_bytes is dst_bytes (a copy) or 2 * dst_bytes (each
+ * written 16-byte piece is the XOR of two read ones).  The 1x128 quantizer is
+ * a 2:1 read:write stream and the transposing requantizer a 1:1 stream; the
+ * benchmark sets them against this.
+ *   src, dst : DEVICE pointers, 16-byte aligned, not overlapping.
+ * Requires dst_bytes >= 0, dst_bytes % 16 == 0.
+ */
+fp8bs_status fp8bs_stream_reference(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
                                     fp8bs_stream_t stream);
 
 /*
