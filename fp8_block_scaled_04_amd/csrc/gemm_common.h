@@ -73,6 +73,13 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
+// s_waitcnt lgkmcnt(0) (this wave's LDS reads and writes are done), then
+// s_barrier: what any wave wrote to LDS before it is visible to every wave
+// after it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p);
 }

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_pp(const GemmArgs p) {
   constexpr int ES = OUT_F32 ? 4 : 2;                 // bytes per output
   constexpr int RSTR = BN * ES + 16;                  // LDS row stride (padded)
   static_assert(BM * RSTR <= C::LDS_BYTES, "the output tile fits in LDS");
-  __builtin_amdgcn_s_barrier();                       // every wave is done with the stages
+  lds_barrier();                                      // every wave is done with the stages
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
     const int col = b_row0 + 16 * i + 4 * fg;
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_pp(const GemmArgs p) {
       }
     }
   }
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   constexpr int CPR = BN * ES / 16;                   // 16-byte pieces per row
   const int64_t rows = min<int64_t>(m_valid - m0, BM);
   const int64_t cols = min<int64_t>(N - n0, BN);      // a multiple of 8 (N % 16 == 0)
