@@ -148,6 +148,7 @@ def extra_kernels(fb, synth):
                       ("quantize_dual_8192x7168", "1to1")):
         r = out[f"reference_stream_{ref}_{M * K / 1e6:.1f}MB_written"]
         out[name]["frac_of_stream_reference"] = out[name]["GBs"] / r["GBs"]
+    stream_2to1_GBs = out[f"reference_stream_2to1_{M * K / 1e6:.1f}MB_written"]["GBs"]
     # The code-only 128x128 block transpose of the same 8192 x 7168 codes
     # (the transpose-requantizer's access pattern, no arithmetic).
     sw = [torch.ones((1, M // 128, K // 128), device="cuda") for _ in range(R)]
@@ -185,7 +186,15 @@ def extra_kernels(fb, synth):
     G, Mt, N, K = 8, 8192, 4096, 7168
     w = synth.contiguous(G, Mt, N, K, seed=0)
     a, sa = fb.quantize_1x128(dev_bf16(w["a"]))
-    b, sb = fb.quantize_128x128(dev_bf16(w["b"]))
+    wb = dev_bf16(w["b"])
+    b, sb = fb.quantize_128x128(wb)
+    # the experts' 128x128 weight quantization (a 2:1 read:write stream of 705 MB)
+    us, how = time_graph(lambda: fb.quantize_128x128(wb, out=(b, sb)))
+    byt = 3 * G * N * K + 4 * G * (N // 128) * (K // 128)
+    out[f"quantize_128x128_{G}x{N}x{K}"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
+                                                frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt,
+                                                frac_of_stream_reference=byt / us / 1e3 / stream_2to1_GBs)
+    del wb
     offs = torch.from_numpy(w["m_offsets"]).cuda()
     us, how = time_graph(lambda: fb.grouped_gemm_contiguous(a, sa, b, sb, offs))
     out["grouped_contiguous_8x8192x4096x7168"] = dict(us=us, timing=how, TFLOPs=2 * Mt * N * K / us / 1e6,
@@ -238,7 +247,19 @@ def extra_kernels(fb, synth):
     # the weight gradient dW = dY^T X from the transposed activations
     T, NO, NI = 4096, 2112, 7168
     w = synth.dense(T, NO, NI, seed=0)
-    wq, ws = fb.quantize_128x128(dev_bf16(w["b"]))
+    wbits = dev_bf16(w["b"])
+    wq, ws = fb.quantize_128x128(wbits)
+    # the projection weight's 128x128 quantization (2:1 read:write)
+    R = rotation(3 * NO * NI)
+    wsrc = [wbits] + [wbits.clone() for _ in range(R - 1)]
+    wdst = [fb.quantize_128x128(x) for x in wsrc]
+    it = iter(range(10 ** 9))
+    us, how = time_graph(lambda: (lambda i: fb.quantize_128x128(wsrc[i % R], out=wdst[i % R]))(next(it)))
+    byt = 3 * NO * NI + 4 * ((NO + 127) // 128) * (NI // 128)
+    out[f"quantize_128x128_{NO}x{NI}"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
+                                              frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt,
+                                              frac_of_stream_reference=byt / us / 1e3 / stream_2to1_GBs)
+    del wsrc, wdst, wbits
     R = rotation(2 * NO * NI)
     wsets = [(wq.clone(), ws.clone()) for _ in range(R)]
     it = iter(range(10 ** 9))

@@ -156,16 +156,25 @@ def quantize_dual(x: torch.Tensor, pow2: bool = False):
     return q, s, qt, st
 
 
-def quantize_128x128(w: torch.Tensor, pow2: bool = False):
+def quantize_128x128(w: torch.Tensor, pow2: bool = False, out=None):
     """BF16 weights w[N][K] or w[G][N][K] -> (q, s) with one scale per 128x128
-    block: s[ceil(N/128)][K/128] (or [G][...])."""
+    block: s[ceil(N/128)][K/128] (or [G][...]).  out=(q, s) writes into the
+    caller's tensors."""
     _need(w, "w", torch.bfloat16)
     if w.dim() not in (2, 3):
         raise ValueError("w must be [N][K] or [G][N][K]")
     G, N, K = (1, *w.shape) if w.dim() == 2 else w.shape
-    q = torch.empty(w.shape, dtype=torch.float8_e4m3fn, device=w.device)
     sshape = ((N + 127) // 128, K // 128) if w.dim() == 2 else (G, (N + 127) // 128, K // 128)
-    s = torch.empty(sshape, dtype=torch.float32, device=w.device)
+    if out is None:
+        q = torch.empty(w.shape, dtype=torch.float8_e4m3fn, device=w.device)
+        s = torch.empty(sshape, dtype=torch.float32, device=w.device)
+    else:
+        q, s = out
+        _codes(q, "q")
+        _need(q, "q")
+        _need(s, "s", torch.float32)
+        if tuple(q.shape) != tuple(w.shape) or tuple(s.shape) != sshape:
+            raise ValueError("out has the wrong shapes")
     _check(_q128(_ptr(w), G, N, K, _ptr(q), _ptr(s), SCALE_POW2 if pow2 else 0, _stream(w)),
            "quantize_128x128")
     return q, s

@@ -117,7 +117,10 @@ def test_transpose_requant_full_size():
     check_transpose(q, s, False, "t128x1 8192x7168")
 
 
-@pytest.mark.parametrize("G,N,K", [(1, 256, 384), (1, 200, 256), (3, 64, 128), (1, 2112, 512), (2, 16, 1024)])
+# ragged last blocks of 72, 64, 3 (not a multiple of the 4 rows one load
+# instruction spans) and 1 rows; the projection weight at full size
+@pytest.mark.parametrize("G,N,K", [(1, 256, 384), (1, 200, 256), (3, 64, 128), (1, 2112, 512), (2, 16, 1024),
+                                   (2, 131, 256), (1, 129, 128), (1, 2112, 7168)])
 @pytest.mark.parametrize("pow2", [False, True])
 def test_quantize_128x128(G, N, K, pow2):
     print(f"quantize_128x128 G={G} N={N} K={K} pow2={pow2}", flush=True)
@@ -129,6 +132,20 @@ def test_quantize_128x128(G, N, K, pow2):
     q_ref, s_ref = quantize.quantize_128x128(w, pow2)
     assert_codes_equal(codes_host(q), q_ref, "128x128 codes")
     assert_codes_equal(f32_bits_host(s), s_ref.view(np.uint32), "128x128 scales")
+
+
+def test_quantize_128x128_into_caller_buffers():
+    # out=(q, s): the same bytes as a fresh call, written over sentinel contents
+    w = bf16_dev(synth.contiguous(2, 128, 200, 384, seed=5)["b"])
+    q0, s0 = fp8bs.quantize_128x128(w)
+    q = torch.full((2, 200, 384), 0x55, dtype=torch.uint8, device="cuda")
+    s = torch.full((2, 2, 3), float("nan"), dtype=torch.float32, device="cuda")
+    fp8bs.quantize_128x128(w, out=(q, s))
+    torch.cuda.synchronize()
+    assert_codes_equal(codes_host(q), codes_host(q0), "128x128 codes into out")
+    assert_codes_equal(f32_bits_host(s), f32_bits_host(s0), "128x128 scales into out")
+    with pytest.raises(ValueError):
+        fp8bs.quantize_128x128(w, out=(q[:, :199], s))
 
 
 def test_cast_f32_to_e4m3():
