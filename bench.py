@@ -281,6 +281,9 @@ def extra_kernels(fb, synth):
     x_bits = synth.activation(T, NI, seed=2)["a"]
     ayt, sayt = fb.quantize_transpose_128x1(a, sa)               # dY^T [Np][T] (zero rows past 2112)
     axt, saxt = fb.quantize_transpose_128x1(*fb.quantize_1x128(dev_bf16(x_bits)))   # X^T [NI][T]
+    # the same operands with power-of-two scales, for the scaled-MFMA weight gradient
+    ayt2, sayt2 = fb.quantize_transpose_128x1(*fb.quantize_1x128(dev_bf16(pad), pow2=True), pow2=True)
+    axt2, saxt2 = fb.quantize_transpose_128x1(*fb.quantize_1x128(dev_bf16(x_bits), pow2=True), pow2=True)
     del qt, st, a, sa
     dw = torch.empty((ayt.shape[0], NI), dtype=torch.float32, device="cuda")
     us, how = time_graph(lambda: fb.gemm_wgrad(ayt, sayt, axt, saxt, out=dw))
@@ -289,6 +292,17 @@ def extra_kernels(fb, synth):
     out["gemm_wgrad_2112x7168x4096"] = dict(us=us, timing=how, TFLOPs=2 * NO * NI * T / us / 1e6,
                                             frac_mfma=2 * NO * NI * T / us / 1e6 / FP8_PEAK_TFLOPS,
                                             rows_run=int(ayt.shape[0]))
+    times = {True: [], False: []}
+    for rnd in range(3):   # alternated, as for the dense pair above
+        for hw in ((True, False) if rnd % 2 == 0 else (False, True)):
+            us2, how2 = time_graph(lambda: (fb.gemm_wgrad(ayt2, sayt2, axt2, saxt2, out=dw, pow2_scales=True) if hw
+                                            else fb.gemm_wgrad(ayt2, sayt2, axt2, saxt2, out=dw)))
+            times[hw].append(us2)
+    for hw in (True, False):
+        us2 = float(np.median(times[hw]))
+        out[f"gemm_wgrad_pow2_{'hw' if hw else 'sw'}_2112x7168x4096"] = dict(
+            us=us2, timing=how2 + ", alternated", TFLOPs=2 * NO * NI * T / us2 / 1e6,
+            frac_mfma=2 * NO * NI * T / us2 / 1e6 / FP8_PEAK_TFLOPS)
     return out
 
 

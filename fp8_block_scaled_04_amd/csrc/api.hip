@@ -182,15 +182,18 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const
 }
 
 fp8bs_status fp8bs_gemm_fp8_wgrad(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, float* d,
-                                  int64_t M, int64_t N, int64_t K, int32_t accumulate, fp8bs_stream_t stream) {
+                                  int64_t M, int64_t N, int64_t K, int32_t accumulate, uint32_t flags,
+                                  fp8bs_stream_t stream) {
   if (M < 0) return FP8BS_ERR_SHAPE;
   if (fp8bs_status e = gemm_common(N, K, FP8BS_OUT_FP32)) return e;
   if (!grid_fits(M, N, 1) || !buffers_fit(M, N, K, true)) return FP8BS_ERR_SHAPE;
   if (accumulate != 0 && accumulate != 1) return FP8BS_ERR_FLAGS;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
   if (M == 0 || N == 0) return FP8BS_OK;
   if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, nullptr, false)) return e;
   if (fp8bs_status e = check_device()) return e;
-  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, true, accumulate == 1, false, fp8bs::kWgrad};
+  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, true, accumulate == 1, (flags & FP8BS_SCALE_POW2) != 0,
+                fp8bs::kWgrad};
   (void)hipGetLastError();
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
 }
@@ -236,7 +239,6 @@ fp8bs_status fp8bs_gemm_tile(int32_t layout, int64_t rows, int64_t N, int64_t K,
   if (layout == 1 && rows % 128) return FP8BS_ERR_SHAPE;
   if (!grid_fits(rows, N, layout == 2 ? G : 1) || !buffers_fit(rows, N, K, layout == 3)) return FP8BS_ERR_SHAPE;
   if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
-  if (layout == 3 && flags) return FP8BS_ERR_FLAGS;
   if (!tile_m || !tile_n || !ping_pong) return FP8BS_ERR_NULL;
   static const fp8bs::GemmMode modes[4] = {fp8bs::kDense, fp8bs::kContiguous, fp8bs::kMasked, fp8bs::kWgrad};
   GemmProblem p{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, rows, N, K, G, false, false,

@@ -404,13 +404,14 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     constexpr bool ROWB = MODE == kWgrad;
     static_assert(!ROWB || C::FM >= 2, "the weight scales are read at a row's second block");
     static_assert(!ROWB || BN <= (C::NW - C::SA_WAVES) * 64, "the scale waves must cover every weight row");
-    static_assert(!(ROWB && HWS), "hardware scaling takes one scale per weight fragment");
     static_assert(!(ROWB && C::CS), "per-row weight scales need every scale slot");
     float4 sbr[3];
     auto sslot = [](int i) { return (i == FN - 1 && (FN - 1) % 2 == 0) ? 2 : i % 2; };
     float sb_lo = 0.f, sb_hi = 0.f;
     int ea[C::FM];              // HWS: this chunk's E8M0 bytes: activation rows (per lane) and
-    int ebf[C::FN];             // the weight block of each weight fragment (uniform, SGPRs)
+    int ebf[C::FN];             // the weight block of each weight fragment (uniform, SGPRs);
+                                // weight gradient: the E8M0 byte of weight row fr of the fragment
+    float sbrow[ROWB && HWS ? C::FN : 1];   // weight gradient, hardware scaling: those rows' scales
     const int blk_lo = sb_idx;
     const int blk_hi = (int)((n0 + b_row0 + C::WN - 1) / 128 - n0 / 128);
     auto read_a1 = [&](int stage, int j) {
@@ -431,6 +432,12 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       for (int j = 0; j < C::FM; ++j) sa[j] = reinterpret_cast<const float*>(st + C::SA_OFF)[a_row0 + 16 * j + fr];
       if (!ROWB) sb_lo = reinterpret_cast<const float*>(st + C::SB_OFF)[blk_lo];
       if (STRADDLE && !ROWB) sb_hi = reinterpret_cast<const float*>(st + C::SB_OFF)[blk_hi];
+      // Weight gradient with hardware scaling: the scaled MFMA takes the
+      // first operand's scale per row (lane fr: weight row b_row0 + 16i + fr)
+      if constexpr (ROWB && HWS)
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i)
+          sbrow[i] = reinterpret_cast<const float*>(st + C::SB_OFF)[b_row0 + 16 * i + fr];
     };
     auto read_sbr = [&](int stage, int i) {
       sbr[sslot(i)] = *reinterpret_cast<const float4*>(smem + stage * C::STAGE + C::SB_OFF + 4 * (b_row0 + 16 * i + 4 * fg));
@@ -492,7 +499,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       for (int b = 1; b < LAST; ++b) {
         const int i = b / C::FM;
         pc[b & 1] = mfma(b);
-        if (ROWB && b % C::FM == 1 && i + 1 < FN) read_sbr(stage, i + 1);
+        if (ROWB && !HWS && b % C::FM == 1 && i + 1 < FN) read_sbr(stage, i + 1);
         if (b % C::FM == 0) {
           if (i + 2 < FN) read_b1(stage, i + 2);
           if (STRADDLE || ROWB) row_scales(i, sc[i & 1]);
@@ -561,7 +568,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       read_b1(nstage, 0);
       __builtin_amdgcn_sched_barrier(0);
       read_sc(nstage);
-      if (ROWB) read_sbr(nstage, 0);
+      if (ROWB && !HWS) read_sbr(nstage, 0);
       __builtin_amdgcn_sched_barrier(0);
       const v4f p3 = mfma(LAST + 3);
       __builtin_amdgcn_sched_barrier(0);
@@ -581,6 +588,11 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
       if constexpr (HWS) {
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) ea[j] = e8m0_of(sa[j]);
+        if constexpr (ROWB) {
+#pragma unroll
+          for (int i = 0; i < C::FN; ++i) ebf[i] = e8m0_of(sbrow[i]);
+          return;
+        }
         const int eb_lo = __builtin_amdgcn_readfirstlane(e8m0_of(sb_lo));
         const int eb_hi = STRADDLE ? __builtin_amdgcn_readfirstlane(e8m0_of(sb_hi)) : eb_lo;
 #pragma unroll
@@ -626,7 +638,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     read_a1(0, 0);
     read_b1(0, 0);
     read_sc(0);
-    if (ROWB) read_sbr(0, 0);
+    if (ROWB && !HWS) read_sbr(0, 0);
 #pragma unroll
     for (int j = 1; j < C::FM; ++j) read_a1(0, j);
     read_b1(0, 1);
@@ -735,8 +747,11 @@ hipError_t launch_cfg(const GemmProblem& pr, hipStream_t stream) {
   a.accumulate = pr.accumulate ? 1 : 0;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * (MODE == kMasked ? pr.G : 1);
   if (blocks == 0) return hipSuccess;
-  if constexpr (MODE == kWgrad) {   // FP32 out, software promotion only
-    hipLaunchKernelGGL((k_gemm<C, MODE, true, false>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
+  if constexpr (MODE == kWgrad) {   // FP32 out
+    if (pr.hw_scale)
+      hipLaunchKernelGGL((k_gemm<C, MODE, true, true>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemm<C, MODE, true, false>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);
   } else if (pr.hw_scale) {
     if (pr.out_f32)
       hipLaunchKernelGGL((k_gemm<C, MODE, true, true>), dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, a);

@@ -42,7 +42,7 @@ _q1x128 = _sig("fp8bs_quantize_1x128", [_P, _I64, _I64, _P, _P, _U32, _P])
 _qt = _sig("fp8bs_quantize_transpose_128x1", [_P, _P, _I64, _I64, _P, _P, _U32, _P])
 _q128 = _sig("fp8bs_quantize_128x128", [_P, _I64, _I64, _I64, _P, _P, _U32, _P])
 _gemm = _sig("fp8bs_gemm_fp8_blockscaled", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _U32, _P])
-_wgrad = _sig("fp8bs_gemm_fp8_wgrad", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P])
+_wgrad = _sig("fp8bs_gemm_fp8_wgrad", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _U32, _P])
 _gcont = _sig("fp8bs_grouped_gemm_fp8_contiguous",
               [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _U32, _P])
 _gmask = _sig("fp8bs_grouped_gemm_fp8_masked",
@@ -231,11 +231,13 @@ def gemm(a, sa, b, sb, out_dtype=torch.bfloat16, out=None, pow2_scales=False):
     return out
 
 
-def gemm_wgrad(a, sa, b, sb, out=None, accumulate=False):
+def gemm_wgrad(a, sa, b, sb, out=None, accumulate=False, pow2_scales=False):
     """Weight gradient D[M][N] (FP32) = A * B^T, K = tokens, both operands with
     one scale per row per 128 K: sa[K/128][M], sb[K/128][N] (the layout the
     transpose-requantize step produces).  With accumulate=True the product is
-    added to `out`."""
+    added to `out`.  pow2_scales=True: every scale is a power of two and the
+    matrix core applies them (outputs that depend on any other scale are
+    NaN)."""
     _codes(a, "a"); _codes(b, "b")
     for t, n in ((a, "a"), (b, "b")):
         _need(t, n, None, 2)
@@ -255,7 +257,8 @@ def gemm_wgrad(a, sa, b, sb, out=None, accumulate=False):
         _need(out, "out", torch.float32, 2)
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
-    _check(_wgrad(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, 1 if accumulate else 0, _stream(a)),
+    _check(_wgrad(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, 1 if accumulate else 0,
+                  SCALE_POW2 if pow2_scales else 0, _stream(a)),
            "gemm_fp8_wgrad")
     return out
 

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 4
+#define FP8BS_ABI_VERSION 5
 
 /* Same type as hipStream_t; declared here so the header needs no HIP headers. */
 struct ihipStream_t;
@@ -214,13 +214,19 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa,
  *   b  : E4M3 [N][K],   sb : FP32 [K/128][N]     (e.g. X^T:  N = input features)
  *   d  : FP32 [M][N]; accumulate = 1 adds the product to d's contents
  *        (gradient accumulation), 0 overwrites them.
+ *   flags : 0, or FP8BS_SCALE_POW2: every scale is a power of two 2^e with
+ *        -127 <= e <= 127 and the scaled MFMA applies both operands' row
+ *        scales itself (page 2, paragraph on MMA with per-group scaling);
+ *        outputs that depend on any other scale are NaN, as for the dense
+ *        GEMM.
  * Requires M >= 0, N >= 0, N % 16 == 0, K > 0, K % 128 == 0, accumulate in
- * {0, 1} (else FP8BS_ERR_FLAGS).
+ * {0, 1} and flags in {0, FP8BS_SCALE_POW2} (else FP8BS_ERR_FLAGS).
  */
 fp8bs_status fp8bs_gemm_fp8_wgrad(const uint8_t* a, const float* sa,
                                   const uint8_t* b, const float* sb,
                                   float* d, int64_t M, int64_t N, int64_t K,
-                                  int32_t accumulate, fp8bs_stream_t stream);
+                                  int32_t accumulate, uint32_t flags,
+                                  fp8bs_stream_t stream);
 
 /*
  * Grouped GEMM, contiguous MoE layout (page 4, section "Schluesselmerkmale

@@ -171,7 +171,7 @@ def test_cast_validation(lib):
 def test_binding_imports_and_reports_its_library(lib_path):
     from fp8_block_scaled_04_amd import fp8bs
     assert fp8bs.library() == lib_path
-    assert fp8bs.abi_version() == 4
+    assert fp8bs.abi_version() == 5
 
 
 def test_package_exports_every_binding_function(lib_path):
@@ -189,16 +189,17 @@ def test_package_exports_every_binding_function(lib_path):
 
 
 def test_wgrad_validation(lib):
-    f = fn(lib, "fp8bs_gemm_fp8_wgrad", [P, P, P, P, P, I64, I64, I64, I32, P])
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 24, 128, 0, None) == SHAPE     # N % 16
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 100, 0, None) == SHAPE     # K % 128
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 32, 128, 0, None) == SHAPE
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 2, None) == FLAGS     # accumulate in {0, 1}
-    assert f(None, None, None, None, None, 0, 32, 128, 0, None) == OK        # empty
-    assert f(FAKE, FAKE, None, FAKE, FAKE, 4, 32, 128, 1, None) == NULL
-    assert f(FAKE, FAKE, FAKE, MIS, FAKE, 4, 32, 128, 0, None) == ALIGN
+    f = fn(lib, "fp8bs_gemm_fp8_wgrad", [P, P, P, P, P, I64, I64, I64, I32, U32, P])
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 24, 128, 0, 0, None) == SHAPE     # N % 16
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 100, 0, 0, None) == SHAPE     # K % 128
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 32, 128, 0, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 2, 0, None) == FLAGS     # accumulate in {0, 1}
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 0, 2, None) == FLAGS     # unknown flag
+    assert f(None, None, None, None, None, 0, 32, 128, 0, 1, None) == OK        # empty
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 4, 32, 128, 1, 0, None) == NULL
+    assert f(FAKE, FAKE, FAKE, MIS, FAKE, 4, 32, 128, 0, 1, None) == ALIGN
     if NO_DEVICE:
-        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 1, None) == DEVICE
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 128, 1, 1, None) == DEVICE
 
 
 def test_transpose_weight_validation(lib):
@@ -237,8 +238,8 @@ def test_gemm_rejects_sizes_beyond_32bit_addressing(lib):
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 256, (1 << 23), 0, 0, None) == SHAPE      # 256*K = 2^31
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 22, 256, 1 << 17, 0, 0, None) == SHAPE    # 4*(K/128)*M = 2^32
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 1 << 28, 1 << 16, 0, 0, None) == SHAPE    # weight block scales
-    w = fn(lib, "fp8bs_gemm_fp8_wgrad", [P] * 5 + [I64] * 3 + [I32, P])
-    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 1 << 22, 1 << 17, 0, None) == SHAPE     # per-row weight scales
+    w = fn(lib, "fp8bs_gemm_fp8_wgrad", [P] * 5 + [I64] * 3 + [I32, U32, P])
+    assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 1 << 22, 1 << 17, 0, 0, None) == SHAPE     # per-row weight scales
     c = fn(lib, "fp8bs_grouped_gemm_fp8_contiguous", [P] * 6 + [I32, I64, I64, I64, I32, U32, P])
     assert c(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1 << 22, 256, 1 << 17, 0, 0, None) == SHAPE
     m = fn(lib, "fp8bs_grouped_gemm_fp8_masked", [P] * 6 + [I32, I64, I64, I64, I32, U32, P])
@@ -259,7 +260,8 @@ def test_gemm_tile_query_validation(lib):
     assert f(0, 128, 256, 512, 2, 0, o, o + 4, o + 8) == SHAPE          # dense takes G = 1
     assert f(1, 100, 256, 512, 2, 0, o, o + 4, o + 8) == SHAPE          # Mt % 128
     assert f(0, 128, 256, 512, 1, 2, o, o + 4, o + 8) == FLAGS
-    assert f(3, 128, 256, 512, 1, 1, o, o + 4, o + 8) == FLAGS          # no pow2 weight gradient
+    assert f(3, 128, 256, 512, 1, 2, o, o + 4, o + 8) == FLAGS          # unknown flag
+    assert f(3, 128, 256, 512, 1, 1, o, o + 4, o + 8) == OK             # power-of-two weight gradient
     assert f(0, 128, 256, 512, 1, 0, None, o + 4, o + 8) == NULL
     assert f(0, 128, 256, 512, 1, 0, o, o + 4, o + 8) == OK and tuple(out) == (128, 96, 0)
 

@@ -100,3 +100,77 @@ def test_wgrad_after_gpu_transpose_chain():
     assert np.array_equal(codes_host(qyt), oyt) and np.array_equal(codes_host(qxt), oxt)
     ref = gemm.wgrad_ref(oyt, osyt, oxt, osxt).astype(np.float64)
     assert_gemm_close(d.cpu().numpy().astype(np.float64), ref, "wgrad chain")
+
+
+# ---- power-of-two scales applied by the scaled MFMA ------------------------
+# Both operands' row scales go to v_mfma_scale_f32_16x16x128_f8f6f4 as E8M0
+# bytes (one per operand row and 128 tokens), which accumulates the scaled
+# chunk product itself: no promotion FMAs.  Same bar as above.
+
+def operands_pow2(M, N, K, seed):
+    a, sa = quantize.quantize_1x128(synth.activation(M, K, seed=seed)["a"], pow2=True)
+    b, sb = quantize.quantize_1x128(synth.activation(N, K, seed=seed + 1)["a"], pow2=True)
+    return a, sa, b, sb
+
+
+def run_pow2(a, sa, b, sb, d_in=None):
+    out = f32_dev(d_in) if d_in is not None else None
+    d = fp8bs.gemm_wgrad(codes_dev(a), f32_dev(sa), codes_dev(b), f32_dev(sb), out=out,
+                         accumulate=d_in is not None, pow2_scales=True)
+    torch.cuda.synchronize()
+    return d.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("M,N,K,tile", [(256, 160, 256, (256, 160)), (300, 208, 384, (256, 160)),
+                                        (1, 16, 128, (256, 160)), (513, 336, 640, (256, 160)),
+                                        (2000, 7008, 384, (256, 256))])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_wgrad_pow2_recipe(M, N, K, tile, accumulate):
+    assert fp8bs.gemm_tile("wgrad", M, N, K, pow2_scales=True)[:2] == tile
+    print(f"pow2 wgrad M={M} N={N} K={K} tile {tile} accumulate={accumulate}", flush=True)
+    a, sa, b, sb = operands_pow2(M, N, K, seed=M + 5 * N + K)
+    d_in = np.random.default_rng(M + N).standard_normal((M, N)).astype(np.float32) if accumulate else None
+    got = run_pow2(a, sa, b, sb, d_in)
+    ref = gemm.wgrad_ref(a, sa, b, sb, d_in).astype(np.float64)
+    assert_gemm_close(got, ref, f"pow2 wgrad {M}x{N}x{K}", dense_allowance(a, sa, b, sb, wgrad=True))
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 320, 1024), (2000, 7008, 384)])
+def test_wgrad_pow2_exact_integer_bit_exact(M, N, K):
+    print(f"pow2 exact-integer wgrad M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(2)
+    vals = e4m3.decode(np.arange(256, dtype=np.uint8))
+    ints = np.array([c for c in range(256) if np.isfinite(vals[c]) and vals[c] == np.round(vals[c])
+                     and abs(vals[c]) <= 16 and c != 0x80], np.uint8)
+    a = rng.choice(ints, (M, K)).astype(np.uint8)
+    b = rng.choice(ints, (N, K)).astype(np.uint8)
+    sa = (2.0 ** rng.integers(-2, 2, (K // 128, M))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-2, 2, (K // 128, N))).astype(np.float32)
+    got = run_pow2(a, sa, b, sb).astype(np.float32)
+    ref = gemm.wgrad_ref(a, sa, b, sb)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_wgrad_pow2_invalid_scale_gives_nan_only_where_used():
+    M, N, K = 300, 208, 384
+    a, sa, b, sb = operands_pow2(M, N, K, seed=8)
+    sa = sa.copy()
+    sb = sb.copy()
+    sa[1, 17] = np.float32(3.0)             # dY^T row 17, tokens 128..255: not a power of two
+    sb[2, 40] = np.float32(0.75)            # X^T row 40, tokens 256..383
+    got = run_pow2(a, sa, b, sb)
+    bad = np.zeros((M, N), bool)
+    bad[17, :] = True
+    bad[:, 40] = True
+    assert np.isnan(got[bad]).all()
+    ref = gemm.wgrad_ref(a, sa, b, sb).astype(np.float64)
+    assert_gemm_close(got[~bad], ref[~bad], "pow2 wgrad outputs with valid scales")
+
+
+def test_wgrad_pow2_projection_size():
+    M, N, K = 2112, 7168, 4096
+    print("pow2 wgrad 2112x7168x4096", flush=True)
+    a, sa, b, sb = operands_pow2(M, N, K, seed=6)
+    got = run_pow2(a, sa, b, sb)
+    ref = gemm.wgrad_ref(a, sa, b, sb).astype(np.float64)
+    assert_gemm_close(got, ref, "pow2 wgrad 2112x7168x4096", dense_allowance(a, sa, b, sb, wgrad=True))
