@@ -131,10 +131,11 @@ def extra_kernels(fb, synth):
     out["quantize_dual_8192x7168"] = dict(us=us, timing=how, GBs=byt / us / 1e3,
                                           frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, bytes=byt)
     # Practical ceilings on this device: the library's streaming reference
-    # (nontemporal 16-byte loads and stores, no arithmetic) writing the same
-    # M*K bytes while reading twice as many (the 1x128 quantizer's mix) or as
-    # many (the transpose-requantizer's).  Each quantizer's line carries its
-    # fraction of the matching stream's rate.
+    # (nontemporal 16-byte loads, no arithmetic) writing the same M*K bytes
+    # while reading twice as many (the 1x128 quantizer's mix, 8-byte stores)
+    # or as many (the transpose-requantizer's, 16-byte nontemporal stores).
+    # Each quantizer's line carries its fraction of the matching stream's
+    # rate.
     srcs = [torch.empty(2 * M * K, dtype=torch.uint8, device="cuda") for _ in range(R)]
     dsts = [torch.empty(M * K, dtype=torch.uint8, device="cuda") for _ in range(R)]
     for ratio in (2, 1):

@@ -1,14 +1,18 @@
-// Streaming reference kernel (not a step of the method): reads `ratio`
-// 16-byte pieces per 16-byte piece written, with nontemporal loads and
-// stores, so the HBM-bound kernels can be set against the throughput a plain
-// stream of the same read:write mix reaches on the same device.  The
-// 1x128 quantizer is a 2:1 stream (BF16 in, codes out), the transposing
+// Streaming reference kernels (not a step of the method): plain streams of
+// the HBM-bound kernels' read:write mixes, so that those can be set against
+// the throughput such a stream reaches on the same device.  The 1x128
+// quantizer is a 2:1 stream (BF16 in, codes out), the transposing
 // requantizer a 1:1 stream.
 //
-// Configuration: 8192 workgroups of 256 lanes walking the output in a
-// grid-stride loop, one piece per lane per step for 1:1 and four for 2:1 (the
-// best of 1/2/4 pieces x 1024..8192 workgroups measured on an MI355X over
-// 58.7 MB outputs: 5.97 TB/s for 1:1, 5.79 TB/s for 2:1).
+// Configuration: 8192 workgroups of 256 lanes walking the data in a
+// grid-stride loop, one piece per lane per step; nontemporal loads.  1:1
+// copies 16-byte pieces with nontemporal stores; 2:1 folds each 16-byte piece
+// read into an 8-byte piece written with ordinary stores.  These were the
+// fastest of the forms measured on an MI355X, with 58.7 MB written, 4096 to
+// 16384 workgroups, and 1, 2 or 4 pieces per lane:
+//   1:1: 6.10 TB/s.  Cached stores gave 5.87, two pieces per lane 5.77.
+//   2:1: 6.51 TB/s.  16-byte nontemporal stores, each the XOR of two pieces
+//        read, gave 5.89.  8-byte nontemporal stores gave 6.27.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -18,46 +22,37 @@ namespace fp8bs {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32x4 ld_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
-// dst piece i = XOR of src pieces RATIO*i .. RATIO*i + RATIO-1.
-template <int U, int RATIO>
-__global__ __launch_bounds__(256) void k_stream(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n16) {
+// 1:1: dst piece i = src piece i (16-byte pieces).
+__global__ __launch_bounds__(256) void k_stream11(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                  int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + (U - 1) * stride < n16; i += U * stride) {
-    u32x4 v[U][RATIO];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < RATIO; ++r) v[u][r] = ld_nt(src + (i + u * stride) * RATIO + r);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      u32x4 w = v[u][0];
-#pragma unroll
-      for (int r = 1; r < RATIO; ++r) w ^= v[u][r];
-      st_nt(dst + i + u * stride, w);
-    }
-  }
-  for (; i < n16; i += stride) {
-    u32x4 w = ld_nt(src + i * RATIO);
-#pragma unroll
-    for (int r = 1; r < RATIO; ++r) w ^= ld_nt(src + i * RATIO + r);
-    st_nt(dst + i, w);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) st_nt(dst + i, ld_nt(src + i));
+}
+
+// 2:1: 8-byte piece i of dst = (w0 ^ w1, w2 ^ w3) of the 32-bit words of
+// 16-byte piece i of src.
+__global__ __launch_bounds__(256) void k_stream21(const u32x4* __restrict__ src, u32x2* __restrict__ dst,
+                                                  int64_t n8) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    const u32x4 v = ld_nt(src + i);
+    dst[i] = u32x2{v.x ^ v.y, v.z ^ v.w};
   }
 }
 
 }  // namespace
 
 hipError_t launch_stream_reference(const void* src, void* dst, int64_t dst_bytes, int ratio, hipStream_t stream) {
-  const int64_t n16 = dst_bytes / 16;
   const dim3 grid(8192), block(256);
   if (ratio == 1)
-    hipLaunchKernelGGL((k_stream<1, 1>), grid, block, 0, stream, (const u32x4*)src, (u32x4*)dst, n16);
+    hipLaunchKernelGGL(k_stream11, grid, block, 0, stream, (const u32x4*)src, (u32x4*)dst, dst_bytes / 16);
   else
-    hipLaunchKernelGGL((k_stream<4, 2>), grid, block, 0, stream, (const u32x4*)src, (u32x4*)dst, n16);
+    hipLaunchKernelGGL(k_stream21, grid, block, 0, stream, (const u32x4*)src, (u32x2*)dst, dst_bytes / 8);
   return hipGetLastError();
 }
 

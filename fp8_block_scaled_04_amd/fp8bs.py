@@ -342,9 +342,9 @@ def gemm_tile(layout: str, rows: int, N: int, K: int, G: int = 1, pow2_scales: b
 
 
 def stream_reference(src: torch.Tensor, dst: torch.Tensor):
-    """Bandwidth reference (not part of the method): stream src into dst with
-    nontemporal loads and stores; src holds as many bytes as dst (a copy) or
-    twice as many (2:1 read:write)."""
+    """Bandwidth reference (not part of the method): stream src into dst; src
+    holds as many bytes as dst (a copy) or twice as many (2:1 read:write: each
+    16-byte piece of src folds into an 8-byte piece of dst)."""
     for t, nm in ((src, "src"), (dst, "dst")):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{nm} must be a contiguous device tensor")

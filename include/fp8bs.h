@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 5
+#define FP8BS_ABI_VERSION 6
 
 /* Same type as hipStream_t; declared here so the header needs no HIP headers. */
 struct ihipStream_t;
@@ -284,9 +284,10 @@ fp8bs_status fp8bs_cast_f32_to_e4m3(const float* x, int64_t n, uint8_t* q,
 
 /*
  * Bandwidth reference (not a step of the method): streams src to dst with
- * nontemporal 16-byte loads and stores, reading src_bytes and writing
- * dst_bytes, where src_bytes is dst_bytes (a copy) or 2 * dst_bytes (each
- * written 16-byte piece is the XOR of two read ones).  The 1x128 quantizer is
+ * nontemporal 16-byte loads, reading src_bytes and writing dst_bytes, where
+ * src_bytes is dst_bytes (a copy, nontemporal 16-byte stores) or
+ * 2 * dst_bytes (8-byte piece i of dst = (w0 ^ w1, w2 ^ w3) of the 32-bit
+ * words of 16-byte piece i of src, ordinary stores).  The 1x128 quantizer is
  * a 2:1 read:write stream and the transposing requantizer a 1:1 stream; the
  * benchmark sets them against this.
  *   src, dst : DEVICE pointers, 16-byte aligned, not overlapping.

@@ -171,7 +171,7 @@ def test_cast_validation(lib):
 def test_binding_imports_and_reports_its_library(lib_path):
     from fp8_block_scaled_04_amd import fp8bs
     assert fp8bs.library() == lib_path
-    assert fp8bs.abi_version() == 5
+    assert fp8bs.abi_version() == 6
 
 
 def test_package_exports_every_binding_function(lib_path):
