@@ -258,6 +258,30 @@ def extra_kernels(fb, synth):
 
     # backward of the 7168 -> 2112 projection over 4096 tokens: weight
     # transposed for the data gradient, dX = dY W (K padded 2112 -> 2176), and
+    # GEMM on a BF16 activation with the 1x128 quantization in its operand
+    # load, against the two steps it replaces (quantize_1x128, then the GEMM):
+    # one or two 128-column tiles per row block (8192 x 128, 16384 x 256), and
+    # the projection shape, whose 17 column tiles each quantize the activation
+    # rows again.
+    for (M, N, K) in ((8192, 128, 7168), (16384, 256, 7168), (4096, 2112, 7168)):
+        w = synth.dense(M, N, K, seed=0)
+        b, sb = fb.quantize_128x128(dev_bf16(w["b"]))
+        x0 = dev_bf16(w["a"])
+        del w
+        R = rotation(3 * M * K)
+        xs = [x0] + [x0.clone() for _ in range(R - 1)]
+        d = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        it = iter(range(10 ** 9))
+        us_f, how = time_graph(lambda: fb.gemm_fused_quantize(xs[next(it) % R], b, sb, out=d))
+        it = iter(range(10 ** 9))
+        us_2, _ = time_graph(lambda: (lambda q: fb.gemm(q[0], q[1], b, sb, out=d))(fb.quantize_1x128(xs[next(it) % R])))
+        flop = 2 * M * N * K
+        out[f"gemm_fused_quantize_{M}x{N}x{K}"] = dict(
+            us=us_f, timing=how, TFLOPs=flop / us_f / 1e6, frac_mfma=flop / us_f / 1e6 / FP8_PEAK_TFLOPS,
+            two_step_us=us_2, speedup_vs_two_step=us_2 / us_f)
+        del xs, x0, d, b, sb
+        torch.cuda.empty_cache()
+
     # the weight gradient dW = dY^T X from the transposed activations
     T, NO, NI = 4096, 2112, 7168
     w = synth.dense(T, NO, NI, seed=0)

@@ -181,6 +181,25 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
 }
 
+fp8bs_status fp8bs_gemm_fused_quantize(const void* x, const uint8_t* b, const float* sb, void* d, int64_t M, int64_t N,
+                                       int64_t K, int32_t out_dtype, uint32_t flags, fp8bs_stream_t stream) {
+  if (M < 0) return FP8BS_ERR_SHAPE;
+  if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
+  // 64-row tiles; the BF16 panel of a tile is 128 * K bytes, below the 256-row
+  // code panel buffers_fit bounds.
+  if (((M + 63) / 64) * ((N + 127) / 128) >= (int64_t(1) << 30) || !buffers_fit(0, N, K, false))
+    return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (!x || !b || !sb || !d) return FP8BS_ERR_NULL;
+  if (!aligned16(x) || !aligned16(b) || !aligned16(sb) || !aligned16(d)) return FP8BS_ERR_ALIGN;
+  if (fp8bs_status e = check_device()) return e;
+  GemmProblem p{static_cast<const uint8_t*>(x), nullptr, b, sb, d, nullptr, M, N, K, 1,
+                out_dtype == FP8BS_OUT_FP32, false, false, fp8bs::kDense};
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_gemm_qa(p, (flags & FP8BS_SCALE_POW2) != 0, (hipStream_t)stream));
+}
+
 fp8bs_status fp8bs_gemm_fp8_wgrad(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, float* d,
                                   int64_t M, int64_t N, int64_t K, int32_t accumulate, uint32_t flags,
                                   fp8bs_stream_t stream) {
@@ -232,9 +251,20 @@ fp8bs_status fp8bs_grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, co
 
 fp8bs_status fp8bs_gemm_tile(int32_t layout, int64_t rows, int64_t N, int64_t K, int32_t G, uint32_t flags,
                              int32_t* tile_m, int32_t* tile_n, int32_t* ping_pong) {
-  if (layout < 0 || layout > 3) return FP8BS_ERR_FLAGS;
+  if (layout < 0 || layout > 4) return FP8BS_ERR_FLAGS;
   if (fp8bs_status e = gemm_common(N, K, FP8BS_OUT_BF16)) return e;
   if (rows < 0 || G < 0) return FP8BS_ERR_SHAPE;
+  if (layout == 4) {   // fp8bs_gemm_fused_quantize
+    if (G != 1) return FP8BS_ERR_SHAPE;
+    if (((rows + 63) / 64) * ((N + 127) / 128) >= (int64_t(1) << 30) || !buffers_fit(0, N, K, false))
+      return FP8BS_ERR_SHAPE;
+    if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
+    if (!tile_m || !tile_n || !ping_pong) return FP8BS_ERR_NULL;
+    *tile_m = 64;
+    *tile_n = fp8bs::gemm_qa_tile_n(N);
+    *ping_pong = 0;
+    return FP8BS_OK;
+  }
   if ((layout == 0 || layout == 3) && G != 1) return FP8BS_ERR_SHAPE;
   if (layout == 1 && rows % 128) return FP8BS_ERR_SHAPE;
   if (!grid_fits(rows, N, layout == 2 ? G : 1) || !buffers_fit(rows, N, K, layout == 3)) return FP8BS_ERR_SHAPE;

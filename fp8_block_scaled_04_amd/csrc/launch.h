@@ -52,5 +52,10 @@ void gemm_tile(const GemmProblem& p, int32_t& bm, int32_t& bn, int32_t& pp);
 // The ping-pong kernel on 192x192 tiles (dense and contiguous layouts; the
 // rows of sA must be a multiple of 4).
 hipError_t launch_gemm_pp192(const GemmProblem& p, hipStream_t stream);
+// The GEMM with a BF16 activation quantized 1x128 in its operand load (dense
+// layout; p.a is the BF16 activation, p.sa unused; pow2: power-of-two tile
+// scales), and the column tile it runs on (64 rows x that).
+hipError_t launch_gemm_qa(const GemmProblem& p, bool pow2, hipStream_t stream);
+int32_t gemm_qa_tile_n(int64_t N);
 
 }  // namespace fp8bs

@@ -97,6 +97,16 @@ __device__ __forceinline__ float div_rn(float x, float s, float r) {
   return __builtin_fmaf(-t, r, q);
 }
 
+// fl32(x / ss), the quotient every quantizer encodes.  With power-of-two
+// scales r = 1/ss is exact (ss lies in [2^-85, 2^120], so r is a normal power
+// of two) and x * r rounds the same real number x / ss once: one multiply
+// gives the correctly rounded quotient, subnormal results and signed zeros
+// included.
+template <bool POW2>
+__device__ __forceinline__ float quot(float x, const TileScale& t) {
+  return POW2 ? x * t.r : div_rn(x, t.ss, t.r);
+}
+
 // ---------------------------------------------------------------------------
 // E4M3 encode (hardware OCP-FP8 conversion, round to nearest even), four
 // values into one dword, byte i = value i.

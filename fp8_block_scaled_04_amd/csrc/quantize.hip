@@ -130,14 +130,6 @@ __device__ __forceinline__ float row_max2(const float (&am)[2], int lane) {
 // consecutive rows are written together (s is [K/128][M], M contiguous).
 // ---------------------------------------------------------------------------
 
-// fl32(x / ss).  With power-of-two scales r = 1/ss is exact (ss lies in
-// [2^-85, 2^120], so r is a normal power of two) and x * r rounds the same
-// real number x / ss once: one multiply gives the correctly rounded quotient,
-// subnormal results and signed zeros included.
-template <bool POW2>
-__device__ __forceinline__ float quot(float x, const TileScale& t) {
-  return POW2 ? x * t.r : div_rn(x, t.ss, t.r);
-}
 
 template <bool POW2, bool SCALED>
 __device__ __forceinline__ uint2 quantize8(uint4 v, const TileScale& t) {

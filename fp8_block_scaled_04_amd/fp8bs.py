@@ -52,6 +52,7 @@ _t128 = _sig("fp8bs_transpose_128x128", [_P, _P, _I64, _I64, _I64, _P, _P, _P])
 _qdual = _sig("fp8bs_quantize_dual", [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P])
 _gtile = _sig("fp8bs_gemm_tile", [_I32, _I64, _I64, _I64, _I32, _U32, _P, _P, _P])
 _sref = _sig("fp8bs_stream_reference", [_P, _I64, _P, _I64, _P])
+_gfq = _sig("fp8bs_gemm_fused_quantize", [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _U32, _P])
 _lib.fp8bs_status_str.argtypes = [ctypes.c_int]
 _lib.fp8bs_status_str.restype = ctypes.c_char_p
 _lib.fp8bs_abi_version.argtypes = []
@@ -231,6 +232,33 @@ def gemm(a, sa, b, sb, out_dtype=torch.bfloat16, out=None, pow2_scales=False):
     return out
 
 
+def gemm_fused_quantize(x, b, sb, out_dtype=torch.bfloat16, out=None, pow2=False):
+    """D[M][N] = Q(x) * B^T for a BF16 activation x[M][K], Q being the 1x128
+    quantization of quantize_1x128 (pow2: power-of-two tile scales), done in
+    the GEMM's operand load; equal bit for bit to quantize_1x128 then gemm
+    with pow2_scales=False.  b: codes [N][K], sb[ceil(N/128)][K/128]."""
+    _need(x, "x", torch.bfloat16, 2)
+    _codes(b, "b")
+    _need(b, "b", None, 2)
+    _need(sb, "sb", torch.float32, 2)
+    M, K = x.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("x and b must share K")
+    if tuple(sb.shape) != ((N + 127) // 128, K // 128):
+        raise ValueError(f"sb must have shape {((N + 127) // 128, K // 128)}, got {tuple(sb.shape)}")
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        _need(out, "out", out_dtype, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    _check(_gfq(_ptr(x), _ptr(b), _ptr(sb), _ptr(out), M, N, K, code, SCALE_POW2 if pow2 else 0, _stream(x)),
+           "gemm_fused_quantize")
+    return out
+
+
 def gemm_wgrad(a, sa, b, sb, out=None, accumulate=False, pow2_scales=False):
     """Weight gradient D[M][N] (FP32) = A * B^T, K = tokens, both operands with
     one scale per row per 128 K: sa[K/128][M], sb[K/128][N] (the layout the
@@ -327,13 +355,14 @@ def cast_to_e4m3(x: torch.Tensor) -> torch.Tensor:
     return q
 
 
-GEMM_LAYOUTS = {"dense": 0, "contiguous": 1, "masked": 2, "wgrad": 3}
+GEMM_LAYOUTS = {"dense": 0, "contiguous": 1, "masked": 2, "wgrad": 3, "fused_quantize": 4}
 
 
 def gemm_tile(layout: str, rows: int, N: int, K: int, G: int = 1, pow2_scales: bool = False):
-    """(tile_m, tile_n, ping_pong) the GEMM call of `layout` ("dense",
-    "contiguous", "masked", "wgrad") would run on; host-side, no device work.
-    rows is M, Mt or cap."""
+    """(tile_m, tile_n, loop) the GEMM call of `layout` ("dense",
+    "contiguous", "masked", "wgrad", "fused_quantize") would run on;
+    host-side, no device work.  rows is M, Mt or cap; loop is 1 for the
+    ping-pong main loop, else 0."""
     out = (ctypes.c_int32 * 3)()
     base = ctypes.addressof(out)
     _check(_gtile(GEMM_LAYOUTS[layout], rows, N, K, G, SCALE_POW2 if pow2_scales else 0,

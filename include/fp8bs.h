@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 6
+#define FP8BS_ABI_VERSION 7
 
 /* Same type as hipStream_t; declared here so the header needs no HIP headers. */
 struct ihipStream_t;
@@ -205,6 +205,31 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa,
                                         fp8bs_stream_t stream);
 
 /*
+ * Dense block-scaled FP8 GEMM on a BF16 activation, quantized on the way in
+ * (page 2, "A Deadly Mistake Uncovered on Deepseek China Ai", paragraph on
+ * hardware suggestions: cast to FP8 during the move from global to shared
+ * memory; page 1, paragraph on 1x128 activation tiles).
+ * D = Q(x) * B^T, where Q(x) is what fp8bs_quantize_1x128 makes of x (same
+ * codes and tile scales, power-of-two scales with FP8BS_SCALE_POW2); the
+ * result equals fp8bs_quantize_1x128 followed by fp8bs_gemm_fp8_blockscaled
+ * with flags 0, bit for bit.  The codes are not stored.  Every 64 x 128
+ * output tile quantizes its activation rows itself, so the call pays off
+ * where few column tiles share them (small N).
+ *   x  : BF16 [M][K]                                      (input)
+ *   b  : E4M3 [N][K],   sb : FP32 [ceil(N/128)][K/128]    (128x128 blocks)
+ *   d  : [M][N], BF16 (out_dtype = FP8BS_OUT_BF16) or FP32 (FP8BS_OUT_FP32)
+ *   flags : 0, or FP8BS_SCALE_POW2 (the activation's tile scales rounded up
+ *           to powers of two; the promotion stays in software)
+ * Requires M >= 0, N >= 0, N % 16 == 0, K > 0, K % 128 == 0, 256 * K < 2^31
+ * and 4 * (K/128) * ceil(N/128) < 2^31; larger problems return
+ * FP8BS_ERR_SHAPE.  Pointers as for fp8bs_gemm_fp8_blockscaled.
+ */
+fp8bs_status fp8bs_gemm_fused_quantize(const void* x, const uint8_t* b, const float* sb,
+                                       void* d, int64_t M, int64_t N, int64_t K,
+                                       int32_t out_dtype, uint32_t flags,
+                                       fp8bs_stream_t stream);
+
+/*
  * Weight-gradient GEMM (page 1, paragraphs on caching FP8 activations and on
  * converting 1x128 tiles to 128x1 tiles for the backward pass): dW = dY^T X
  * contracts over tokens, so both operands carry one scale per row per 128
@@ -300,8 +325,10 @@ fp8bs_status fp8bs_stream_reference(const void* src, int64_t src_bytes, void* ds
  * Tile a GEMM call would run on (host-side query: no device, no launch; for
  * tests and tuning, not part of the method the pages describe).
  *   layout : 0 dense (fp8bs_gemm_fp8_blockscaled), 1 contiguous grouped,
- *            2 masked grouped, 3 weight gradient
- *   rows   : M (dense, weight gradient), Mt (contiguous) or cap (masked)
+ *            2 masked grouped, 3 weight gradient, 4 dense on a BF16
+ *            activation (fp8bs_gemm_fused_quantize)
+ *   rows   : M (dense, weight gradient, BF16 activation), Mt (contiguous)
+ *            or cap (masked)
  *   N, K, G, flags : as passed to that call (G = 1 for dense and weight
  *            gradient)
  *   tile_m, tile_n : HOST pointers, receive the output tile (rows x columns

@@ -46,7 +46,7 @@ def lib(lib_path):
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in fp8bs.h but not exported"
 
@@ -171,7 +171,7 @@ def test_cast_validation(lib):
 def test_binding_imports_and_reports_its_library(lib_path):
     from fp8_block_scaled_04_amd import fp8bs
     assert fp8bs.library() == lib_path
-    assert fp8bs.abi_version() == 6
+    assert fp8bs.abi_version() == 7
 
 
 def test_package_exports_every_binding_function(lib_path):
@@ -186,6 +186,22 @@ def test_package_exports_every_binding_function(lib_path):
     assert public == set(pkg.__all__), public ^ set(pkg.__all__)
     for n in pkg.__all__:
         assert getattr(pkg, n) is getattr(fp8bs, n)
+
+
+def test_fused_quantize_validation(lib):
+    f = fn(lib, "fp8bs_gemm_fused_quantize", [P, P, P, P, I64, I64, I64, I32, U32, P])
+    four = [FAKE] * 4
+    assert f(*four, 64, 24, 128, 0, 0, None) == SHAPE             # N % 16
+    assert f(*four, 64, 32, 100, 0, 0, None) == SHAPE             # K % 128
+    assert f(*four, -1, 32, 128, 0, 0, None) == SHAPE
+    assert f(*four, 64, 32, 1 << 24, 0, 0, None) == SHAPE         # 256 * K >= 2^31
+    assert f(*four, 64, 32, 128, 2, 0, None) == FLAGS             # unknown out dtype
+    assert f(*four, 64, 32, 128, 0, 2, None) == FLAGS             # unknown flag
+    assert f(None, None, None, None, 0, 32, 128, 0, 1, None) == OK   # empty
+    assert f(FAKE, None, FAKE, FAKE, 64, 32, 128, 0, 0, None) == NULL
+    assert f(MIS, FAKE, FAKE, FAKE, 64, 32, 128, 1, 0, None) == ALIGN
+    if NO_DEVICE:
+        assert f(*four, 64, 32, 128, 1, 1, None) == DEVICE
 
 
 def test_wgrad_validation(lib):
@@ -254,7 +270,10 @@ def test_gemm_tile_query_validation(lib):
     f = fn(lib, "fp8bs_gemm_tile", [I32, I64, I64, I64, I32, U32, P, P, P])
     out = (ctypes.c_int32 * 3)()
     o = ctypes.addressof(out)
-    assert f(4, 128, 256, 512, 1, 0, o, o + 4, o + 8) == FLAGS          # unknown layout
+    assert f(5, 128, 256, 512, 1, 0, o, o + 4, o + 8) == FLAGS          # unknown layout
+    assert f(4, 128, 256, 512, 2, 0, o, o + 4, o + 8) == SHAPE          # BF16 activation: G = 1
+    assert f(4, 128, 256, 512, 1, 2, o, o + 4, o + 8) == FLAGS
+    assert f(4, 128, 256, 512, 1, 1, None, o + 4, o + 8) == NULL
     assert f(0, 128, 24, 512, 1, 0, o, o + 4, o + 8) == SHAPE           # N % 16
     assert f(0, 128, 256, 500, 1, 0, o, o + 4, o + 8) == SHAPE          # K % 128
     assert f(0, 128, 256, 512, 2, 0, o, o + 4, o + 8) == SHAPE          # dense takes G = 1
@@ -290,6 +309,9 @@ TILES = [
     (("masked", 256, 7168, 2048, 32), (128, 256, 0)),
     (("wgrad", 2112, 7168, 4096), (256, 256, 0)),
     (("wgrad", 300, 208, 384), (256, 160, 0)),
+    (("fused_quantize", 16384, 256, 7168), (64, 128, 0)),
+    (("fused_quantize", 100, 48, 256), (64, 128, 0)),
+    (("fused_quantize", 300, 528, 640, 1, True), (64, 128, 0)),
 ]
 
 
