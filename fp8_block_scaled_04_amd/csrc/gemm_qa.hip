@@ -38,10 +38,10 @@
 namespace fp8bs {
 namespace {
 
-template <int BN_, int S_>
+template <int BM_, int BN_, int S_>
 struct QACfg {
-  static constexpr int BM = 64, BN = BN_;
-  static constexpr int NW = 4, THREADS = 64 * NW;
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int NW = BM / 16, THREADS = 64 * NW;   // one 16-row fragment per wave
   static constexpr int FN = BN / 16;                 // weight fragments per wave
   static constexpr int NG = 4;                       // weight fragments read at a time
   static constexpr int S = S_;                       // LDS stages: the DMA runs S - 1 chunks ahead
@@ -52,6 +52,7 @@ struct QACfg {
   static constexpr int B_DMA = BN * kKC / 1024 / NW;
   static constexpr int DMA = A_DMA + B_DMA;
   static_assert(BN % 128 == 0 && FN % NG == 0, "whole weight blocks and fragment groups");
+  static_assert(A_BYTES % (1024 * NW) == 0 && (BN * kKC) % (1024 * NW) == 0, "whole DMAs per wave");
   static_assert(LDS_BYTES <= 160 * 1024, "the stages fit in LDS");
   static_assert(BM * (BN * 4 + 16) <= LDS_BYTES, "the FP32 output tile fits in the stages");
 };
@@ -76,10 +77,10 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_qa(const GemmArgs p) {
   const int64_t n0 = (int64_t)(pid % p.tiles_n) * BN;
 
   // ---- DMA ------------------------------------------------------------------
-  // Activation instruction j (rows 4j .. 4j+3, j = wave + 4i): lane l takes
-  // row 4j + l/16 into physical segment l % 16, i.e. logical segment
+  // Activation instruction j (rows 4j .. 4j+3, j = wave + NW*i): lane l
+  // takes row 4j + l/16 into physical segment l % 16, i.e. logical segment
   // (l % 16) ^ (row % 16).  Weight instruction j (rows 8j .. 8j+7, j = wave +
-  // 4i): lane l takes row 8j + l/8 into physical segment l % 8, logical
+  // NW*i): lane l takes row 8j + l/8 into physical segment l % 8, logical
   // (l % 8) ^ swz(row).  Rows past M or N read as zeros (range check), chunks
   // past K come from a zero-record descriptor.
   const int64_t a_rows = min<int64_t>(M - m0, BM), b_rows = min<int64_t>(N - n0, BN);
@@ -89,12 +90,12 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_qa(const GemmArgs p) {
   uint32_t a_off[C::A_DMA], b_off[C::B_DMA];
 #pragma unroll
   for (int i = 0; i < C::A_DMA; ++i) {
-    const int row = 4 * (wave + 4 * i) + (lane >> 4);
+    const int row = 4 * (wave + C::NW * i) + (lane >> 4);
     a_off[i] = (uint32_t)(row * K * 2 + 16 * ((lane & 15) ^ (row & 15)));
   }
 #pragma unroll
   for (int i = 0; i < C::B_DMA; ++i) {
-    const int row = 8 * (wave + 4 * i) + (lane >> 3);
+    const int row = 8 * (wave + C::NW * i) + (lane >> 3);
     b_off[i] = (uint32_t)(row * K + 16 * ((lane & 7) ^ swz(row)));
   }
   const uint32_t smem_lds = lds_addr(smem);
@@ -103,10 +104,11 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm_qa(const GemmArgs p) {
     const uint32_t st = smem_lds + (uint32_t)(kb % S) * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::A_DMA; ++i)
-      dma16(in ? ra : r_none, st + 4 * (wave + 4 * i) * 256, a_off[i], in ? (uint32_t)kb * 256 : 0u);
+      dma16(in ? ra : r_none, st + 4 * (wave + C::NW * i) * 256, a_off[i], in ? (uint32_t)kb * 256 : 0u);
 #pragma unroll
     for (int i = 0; i < C::B_DMA; ++i)
-      dma16(in ? rb : r_none, st + C::A_BYTES + 8 * (wave + 4 * i) * kKC, b_off[i], in ? (uint32_t)kb * kKC : 0u);
+      dma16(in ? rb : r_none, st + C::A_BYTES + 8 * (wave + C::NW * i) * kKC, b_off[i],
+            in ? (uint32_t)kb * kKC : 0u);
   };
 
   // ---- fragments ------------------------------------------------------------
@@ -263,7 +265,7 @@ hipError_t launch_qa_cfg(const GemmProblem& pr, bool pow2, hipStream_t stream) {
 
 }  // namespace
 
-using QATile = QACfg<128, 2>;
+using QATile = QACfg<64, 128, 2>;
 
 int32_t gemm_qa_tile_n(int64_t) { return QATile::BN; }
 
