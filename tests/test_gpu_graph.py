@@ -116,3 +116,33 @@ def test_graph_replays_quantizers_and_masked_gemm():
             assert np.array_equal(got[k], want[k]), f"replay {rep}: {k}"
         step()
         torch.cuda.synchronize()
+
+
+def test_graph_replays_fused_quantize_gemm():
+    """The GEMM that quantizes its BF16 activation in the operand load, inside
+    a captured graph: every replay equals the eager call."""
+    M, N, K = 320, 256, 1024
+    print(f"graph capture fused-quantize gemm M={M} N={N} K={K}", flush=True)
+    w = synth.dense(M, N, K, seed=21)
+    x = bf16_dev(w["a"])
+    b, sb = fp8bs.quantize_128x128(bf16_dev(w["b"]))
+    d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    fp8bs.gemm_fused_quantize(x, b, sb, out=d)
+    torch.cuda.synchronize()
+    want = d.view(torch.int16).cpu().numpy().copy()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fp8bs.gemm_fused_quantize(x, b, sb, out=d)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        d.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(d.view(torch.int16).cpu().numpy(), want), f"replay {rep}"
+        fp8bs.gemm_fused_quantize(x, b, sb)      # eager work between replays
+        torch.cuda.synchronize()
