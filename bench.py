@@ -116,9 +116,24 @@ def stream_rate_on(fb, srcs, ratio):
     return (ratio + 1) * n / us / 1e3
 
 
+def progress(msg):
+    """One line on stderr as each part of the run finishes (the JSON record
+    stays the only line on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class _Reported(dict):
+    """The per-kernel table: reports each entry on stderr as it is measured."""
+
+    def __setitem__(self, key, value):
+        super().__setitem__(key, value)
+        us = value.get("us") if isinstance(value, dict) else None
+        progress(f"{key}: {us:.2f} us" if isinstance(us, float) else f"{key}: done")
+
+
 def extra_kernels(fb, synth):
     """Per-kernel measurements on each workload of the hot path."""
-    out = {}
+    out = _Reported()
     # 1x128 quantizer and transpose-requant on the 8192 x 7168 activation
     M, K = 8192, 7168
     x_bits = synth.activation(M, K, seed=0)["a"]
@@ -544,6 +559,7 @@ def main():
     x = dev_bf16(w["a"])
     bq, bs = fb.quantize_128x128(dev_bf16(w["b"]))
     d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    progress(f"workload {M}x{N}x{K} on the device")
 
     def step():
         q, s = fb.quantize_1x128(x)
@@ -593,6 +609,7 @@ def main():
     qv1.record()
     torch.cuda.synchronize()
     quant_us = qv0.elapsed_time(qv1) * 1e3 / args.steps
+    progress(f"{args.steps} timed steps: {ms_per_step * 1e3:.1f} us per step")
     gemm_us = ev0.elapsed_time(ev1) * 1e3 / args.steps - quant_us
     kernel_us_method = "timed steps minus as many quantizer calls, HIP events"
     if not gemm_us > 0:   # the difference of two noisy spans; not expected
@@ -658,6 +675,7 @@ def main():
     if not args.no_extra:
         rec["kernels"] = extra_kernels(fb, synth)
     if not args.no_cpu:
+        progress("oracle on the host cores (cpu_baseline)")
         rec["cpu_baseline"] = cpu_baseline(synth)
     print(json.dumps(rec), flush=True)
 
