@@ -404,10 +404,11 @@ def vs_hipblaslt(fb, synth, reps=5, burst=20):
     return out
 
 
-def cpu_baseline(synth, reps=2):
+def cpu_baseline(synth, reps=8):
     """The CPU oracle on the same step: 1x128 quantization of the whole BF16
-    activation and its GEMM against the quantized weight, run `reps` times,
-    in TFLOP/s of GEMM work per step."""
+    activation and its GEMM against the quantized weight, run `reps` times
+    (about ten seconds of CPU work on a 16-core host), in TFLOP/s of GEMM work
+    per step."""
     from oracle import gemm as og, quantize as oq
     try:
         from threadpoolctl import threadpool_info
