@@ -8,6 +8,7 @@
 
 #include "fp8bs.h"
 #include "launch.h"
+#include "splitk.h"
 
 namespace {
 
@@ -179,6 +180,36 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const
                 (flags & FP8BS_SCALE_POW2) != 0, fp8bs::kDense};
   (void)hipGetLastError();
   return launched(fp8bs::launch_gemm(p, (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_gemm_fp8_blockscaled_splitk(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                               void* d, int64_t M, int64_t N, int64_t K, int32_t out_dtype,
+                                               uint32_t flags, void* workspace, int64_t workspace_bytes,
+                                               fp8bs_stream_t stream) {
+  if (M < 0) return FP8BS_ERR_SHAPE;
+  if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
+  if (!grid_fits(M, N, 1) || !buffers_fit(M, N, K, false)) return FP8BS_ERR_SHAPE;
+  const int64_t need = fp8bs::splitk_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, nullptr, false)) return e;
+  if (need > 0 && !workspace) return FP8BS_ERR_NULL;
+  if (need > 0 && !aligned16(workspace)) return FP8BS_ERR_ALIGN;
+  if (fp8bs_status e = check_device()) return e;
+  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, out_dtype == FP8BS_OUT_FP32, false,
+                (flags & FP8BS_SCALE_POW2) != 0, fp8bs::kDense};
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_gemm_splitk(p, static_cast<float*>(workspace), (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
+  if (M < 0) return FP8BS_ERR_SHAPE;
+  if (fp8bs_status e = gemm_common(N, K, FP8BS_OUT_BF16)) return e;
+  if (!grid_fits(M, N, 1) || !buffers_fit(M, N, K, false)) return FP8BS_ERR_SHAPE;
+  if (!bytes) return FP8BS_ERR_NULL;
+  *bytes = fp8bs::splitk_workspace_bytes(M, N, K);
+  return FP8BS_OK;
 }
 
 fp8bs_status fp8bs_gemm_fused_quantize(const void* x, const uint8_t* b, const float* sb, void* d, int64_t M, int64_t N,

@@ -44,6 +44,7 @@
 //     on the same XCD (own L2), then walked in groups of group_m tile rows
 //     (4 for 256-row tiles, 8 for the smaller ones).
 #include "gemm_common.h"
+#include "splitk.h"
 
 namespace fp8bs {
 namespace {
@@ -153,11 +154,34 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int64_t K = p.K, N = p.N;
-  const int KT = (int)(K / kKC);
+  const int KTS = (int)(K / kKC);   // chunks of the whole K (strides of the weight-scale grid)
+  int KT = KTS;                     // chunks this workgroup runs
   const int64_t NB = (N + 127) / 128;
 
   Tile t;
-  if (!map_tile<BM, BN, MODE>(p, K, KT, NB, t)) return;
+  int split_tile = 0, split = 0, kb0 = 0;
+  if constexpr (MODE == kSplitK) {
+    // Dense, split K: workgroup b runs split b % G (p.G splits) of tile b / G
+    // (tiles column-major over tiles_m row tiles), chunks [kb0, kb1); the
+    // operand and scale bases start at chunk kb0 (row strides unchanged).
+    const int S = p.G;
+    split_tile = (int)blockIdx.x / S;
+    split = (int)blockIdx.x - split_tile * S;
+    kb0 = (int)((int64_t)split * KTS / S);
+    KT = (int)((int64_t)(split + 1) * KTS / S) - kb0;
+    t.a_base = p.a + (int64_t)kb0 * kKC;
+    t.sa_base = p.sa + (int64_t)kb0 * p.M;
+    t.b_base = p.b + (int64_t)kb0 * kKC;
+    t.sb_base = p.sb + kb0;
+    t.m_alloc = p.M;
+    t.m_valid = p.M;
+    t.sa_stride = p.M;
+    t.d_row0 = 0;
+    t.m0 = (int64_t)(split_tile % p.tiles_m) * BM;
+    t.n0 = (int64_t)(split_tile / p.tiles_m) * BN;
+  } else {
+    if (!map_tile<BM, BN, MODE>(p, K, KT, NB, t)) return;
+  }
   const uint8_t* a_base = t.a_base;
   const float* sa_base = t.sa_base;
   const uint8_t* b_base = t.b_base;
@@ -173,7 +197,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   const v4i ra = make_rsrc(a_base + m0 * K, a_rows * K);
   const v4i rb = make_rsrc(b_base + n0 * K, b_rows * K);
   const v4i rsa = make_rsrc(sa_base, KT * sa_stride * 4);
-  const v4i rsb = make_rsrc(sb_base, NB * KT * 4);
+  const v4i rsb = make_rsrc(sb_base, NB * KTS * 4 - (int64_t)kb0 * 4);
 
   // DMA instruction t = i*NW + wave moves rows 8t .. 8t+7 (whole 128-byte
   // lines), lane l taking row 8t + l/8, physical segment l%8, i.e. logical
@@ -210,7 +234,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   const v4i rsb_w = make_rsrc(sb_base, (int64_t)KT * N * 4);
   const v4i rsc = sa_wave ? rsa : (MODE == kWgrad ? rsb_w : rsb);
   const uint32_t sc_voff = sa_wave ? (uint32_t)(sa_row * 4)
-                                   : (MODE == kWgrad ? (uint32_t)(sb_row * 4) : (uint32_t)(sb_blk * KT * 4));
+                                   : (MODE == kWgrad ? (uint32_t)(sb_row * 4) : (uint32_t)(sb_blk * KTS * 4));
   const uint32_t sc_step = __builtin_amdgcn_readfirstlane(
       sa_wave ? (uint32_t)(sa_stride * 4) : (MODE == kWgrad ? (uint32_t)(N * 4) : 4u));
 
@@ -674,6 +698,25 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
   }
   __builtin_amdgcn_s_waitcnt(0);   // every DMA of this wave has landed in LDS
 
+  if constexpr (MODE == kSplitK) {
+    // The tile's FP32 partial over this split's chunks, as a BM x BN block
+    // of the workspace (p.d): the rows inside the matrix (the reduction reads
+    // no others); columns past it hold zeros.
+    float* part = reinterpret_cast<float*>(p.d) + ((int64_t)split_tile * p.G + split) * (BM * BN);
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) {
+      const int row = a_row0 + 16 * j + fr;
+      if (m0 + row < m_valid) {
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) {
+          const v4f& v = acc[i][j];
+          *reinterpret_cast<float4*>(part + row * BN + b_row0 + 16 * i + 4 * fg) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+    return;
+  }
+
   // ---- epilogue: through LDS, then whole rows -----------------------------
   // Lane (fr, fg) holds D[m][n .. n+3] of each fragment: stored from there,
   // every row segment is 32 (BF16) or 64 (FP32) bytes, a part of a cache
@@ -870,7 +913,77 @@ void tile_of(const GemmProblem& p, int32_t& bm, int32_t& bn, int32_t& pp) {
   }
 }
 
+// ---- split K --------------------------------------------------------------
+// D[m][n] = sum over the splits s = 0, 1, .. of partial s of the tile holding
+// (m, n), added in that order (four outputs of one row per lane).
+using SplitTile = StreamTile;
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, void* __restrict__ d, int64_t M,
+                                                       int64_t N, int32_t S, int32_t tiles_m) {
+  constexpr int BM = SplitTile::BM, BN = SplitTile::BN;
+  const int64_t n4 = N / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * n4) return;
+  const int64_t m = idx / n4, c = (idx - m * n4) * 4;
+  const int64_t tile = (c / BN) * tiles_m + m / BM;
+  const float* pp = ws + tile * S * (BM * BN) + (m % BM) * BN + c % BN;
+  float4 v = *reinterpret_cast<const float4*>(pp);
+  for (int s = 1; s < S; ++s) {
+    const float4 w = *reinterpret_cast<const float4*>(pp + (int64_t)s * (BM * BN));
+    v = make_float4(v.x + w.x, v.y + w.y, v.z + w.z, v.w + w.w);
+  }
+  if (OUT_F32) *reinterpret_cast<float4*>(reinterpret_cast<float*>(d) + m * N + c) = v;
+  else *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(d) + m * N + c) = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+}
+
 }  // namespace
+
+// Splits: as many as fill one round of the 256 CUs with the 128x96 tiles
+// (one workgroup per CU), with at least two chunks each and at most 32; only
+// for K of at least 32 chunks, where the split saves more than the second
+// launch and the partials' round trip cost (measured: 64 x 2112 x 7168 28.4
+// -> 15.6 us with 11 splits, 256 x 2112 x 7168 50.4 -> 17.7 us with 5, but
+// 128 x 7168 x 2048, 16 chunks, 13.8 -> 16.8 us with 3).
+int32_t splitk_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + SplitTile::BM - 1) / SplitTile::BM) * ((N + SplitTile::BN - 1) / SplitTile::BN);
+  const int64_t kt = K / kKC;
+  if (tiles <= 0 || kt < 32) return 1;
+  int64_t s = 256 / tiles;
+  s = s > kt / 2 ? kt / 2 : s;
+  s = s > 32 ? 32 : s;
+  return s >= 2 ? (int32_t)s : 1;
+}
+
+int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int32_t s = splitk_splits(M, N, K);
+  if (s < 2) return 0;
+  const int64_t tiles = ((M + SplitTile::BM - 1) / SplitTile::BM) * ((N + SplitTile::BN - 1) / SplitTile::BN);
+  return tiles * s * SplitTile::BM * SplitTile::BN * (int64_t)sizeof(float);
+}
+
+hipError_t launch_gemm_splitk(const GemmProblem& pr, float* ws, hipStream_t stream) {
+  const int32_t S = splitk_splits(pr.M, pr.N, pr.K);
+  if (S < 2) return launch_gemm(pr, stream);
+  GemmArgs a;
+  a.a = pr.a; a.sa = pr.sa; a.b = pr.b; a.sb = pr.sb; a.d = ws; a.groups = nullptr;
+  a.M = pr.M; a.N = pr.N; a.K = pr.K; a.G = S;
+  a.tiles_m = (int32_t)((pr.M + SplitTile::BM - 1) / SplitTile::BM);
+  a.tiles_n = (int32_t)((pr.N + SplitTile::BN - 1) / SplitTile::BN);
+  a.group_m = 8;
+  a.accumulate = 0;
+  const dim3 grid((unsigned)((int64_t)a.tiles_m * a.tiles_n * S)), block(SplitTile::THREADS);
+  if (pr.hw_scale) hipLaunchKernelGGL((k_gemm<SplitTile, kSplitK, true, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((k_gemm<SplitTile, kSplitK, true, false>), grid, block, 0, stream, a);
+  if (hipError_t e = hipGetLastError()) return e;
+  const int64_t outs = pr.M * (pr.N / 4);
+  const dim3 rgrid((unsigned)((outs + 255) / 256)), rblock(256);
+  if (pr.out_f32)
+    hipLaunchKernelGGL(k_splitk_reduce<true>, rgrid, rblock, 0, stream, ws, pr.d, pr.M, pr.N, S, a.tiles_m);
+  else
+    hipLaunchKernelGGL(k_splitk_reduce<false>, rgrid, rblock, 0, stream, ws, pr.d, pr.M, pr.N, S, a.tiles_m);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
   switch (p.mode) {

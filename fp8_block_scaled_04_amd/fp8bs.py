@@ -53,6 +53,9 @@ _qdual = _sig("fp8bs_quantize_dual", [_P, _I64, _I64, _P, _P, _P, _P, _U32, _P])
 _gtile = _sig("fp8bs_gemm_tile", [_I32, _I64, _I64, _I64, _I32, _U32, _P, _P, _P])
 _sref = _sig("fp8bs_stream_reference", [_P, _I64, _P, _I64, _P])
 _gfq = _sig("fp8bs_gemm_fused_quantize", [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _U32, _P])
+_gsplit = _sig("fp8bs_gemm_fp8_blockscaled_splitk",
+               [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _U32, _P, _I64, _P])
+_gsplit_ws = _sig("fp8bs_gemm_splitk_workspace", [_I64, _I64, _I64, _P])
 _lib.fp8bs_status_str.argtypes = [ctypes.c_int]
 _lib.fp8bs_status_str.restype = ctypes.c_char_p
 _lib.fp8bs_abi_version.argtypes = []
@@ -229,6 +232,47 @@ def gemm(a, sa, b, sb, out_dtype=torch.bfloat16, out=None, pow2_scales=False):
     _check(_gemm(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, code,
                  SCALE_POW2 if pow2_scales else 0, _stream(a)),
            "gemm_fp8_blockscaled")
+    return out
+
+
+def splitk_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes gemm_splitk needs for M x N x K (0: it would not split)."""
+    out = ctypes.c_int64(0)
+    _check(_gsplit_ws(M, N, K, ctypes.byref(out)), "gemm_splitk_workspace")
+    return int(out.value)
+
+
+def gemm_splitk(a, sa, b, sb, out_dtype=torch.bfloat16, out=None, pow2_scales=False, workspace=None):
+    """gemm() with the K chunks of each output tile split over several
+    workgroups (for few rows and columns); equal to gemm() up to the order of
+    FP32 additions.  workspace: a uint8 device tensor of at least
+    splitk_workspace_bytes(M, N, K) bytes, allocated here when not given."""
+    _codes(a, "a"); _codes(b, "b")
+    for t, n in ((a, "a"), (b, "b")):
+        _need(t, n, None, 2)
+    _need(sa, "sa", torch.float32, 2)
+    _need(sb, "sb", torch.float32, 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must share K")
+    if tuple(sa.shape) != (K // 128, M) or tuple(sb.shape) != ((N + 127) // 128, K // 128):
+        raise ValueError("scale shapes do not match the operands")
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    else:
+        _need(out, "out", out_dtype, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    need = splitk_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != a.device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on the operands' device")
+    _check(_gsplit(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, code,
+                   SCALE_POW2 if pow2_scales else 0, _ptr(workspace), workspace.numel(), _stream(a)),
+           "gemm_fp8_blockscaled_splitk")
     return out
 
 

@@ -46,7 +46,9 @@
  *     write) unless stated otherwise; data pointers must be 16-byte aligned.
  *   - All tensors are dense row-major with no padding between rows.
  *   - The caller allocates, owns and frees every buffer; the library keeps no
- *     pointer after returning, allocates nothing, and has no workspace.
+ *     pointer after returning and allocates nothing.  The one call that needs
+ *     scratch memory (fp8bs_gemm_fp8_blockscaled_splitk) takes it from the
+ *     caller as a workspace argument.
  *   - Every call enqueues its kernels on `stream` (NULL = the null stream) and
  *     returns without waiting; buffers must stay alive until the stream work
  *     completes.  Calls are re-entrant and thread-safe.
@@ -69,7 +71,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 7
+#define FP8BS_ABI_VERSION 8
 
 /* Same type as hipStream_t; declared here so the header needs no HIP headers. */
 struct ihipStream_t;
@@ -203,6 +205,45 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa,
                                         void* d, int64_t M, int64_t N, int64_t K,
                                         int32_t out_dtype, uint32_t flags,
                                         fp8bs_stream_t stream);
+
+/*
+ * The dense GEMM above with its K chunks split over several workgroups, for
+ * shapes whose output tiles are too few to occupy the GPU: decode-sized
+ * activations against a projection (page 4, "Deepseek veroeffentlicht
+ * Deepgemm", Table 1 "DeepGemm Performance Benchmarks": its row with M = 64,
+ * N = 2112, K = 7168; page 2, paragraph on decoding, where few tokens make the
+ * GEMM memory-bound).  It splits only where K has at least 32 chunks (with at
+ * least two per split).  Each 128 x 96 output tile is computed by S workgroups, one
+ * per range of K chunks, each promoting its chunks into FP32 exactly as the
+ * unsplit GEMM does; the S FP32 partials are then added in split order and
+ * rounded once to the output type.  The result equals the unsplit GEMM's up to
+ * the order of its FP32 additions (bit for bit where those are exact), and is
+ * the same on every run.  Where S would be 1 (fp8bs_gemm_splitk_workspace
+ * reports 0 bytes) the call runs the unsplit GEMM and uses no workspace.
+ *   a, sa, b, sb, d, M, N, K, out_dtype, flags : as fp8bs_gemm_fp8_blockscaled
+ *   workspace       : device scratch of workspace_bytes bytes, at least what
+ *                     fp8bs_gemm_splitk_workspace reports for M, N, K (may be
+ *                     NULL when that is 0); 16-byte aligned.  Its contents on
+ *                     entry do not matter and are overwritten; calls that
+ *                     share a workspace must not overlap in time.
+ *   workspace_bytes : its size
+ * Requires what fp8bs_gemm_fp8_blockscaled requires; a workspace smaller than
+ * needed returns FP8BS_ERR_SHAPE.
+ */
+fp8bs_status fp8bs_gemm_fp8_blockscaled_splitk(const uint8_t* a, const float* sa,
+                                               const uint8_t* b, const float* sb,
+                                               void* d, int64_t M, int64_t N, int64_t K,
+                                               int32_t out_dtype, uint32_t flags,
+                                               void* workspace, int64_t workspace_bytes,
+                                               fp8bs_stream_t stream);
+
+/*
+ * Workspace bytes fp8bs_gemm_fp8_blockscaled_splitk needs for M x N x K
+ * (host-side query, no device): 0 when the call would not split.
+ *   bytes : HOST pointer, receives the size
+ * Requires the sizes fp8bs_gemm_fp8_blockscaled requires.
+ */
+fp8bs_status fp8bs_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes);
 
 /*
  * Dense block-scaled FP8 GEMM on a BF16 activation, quantized on the way in
