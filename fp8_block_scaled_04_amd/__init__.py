@@ -16,8 +16,8 @@ Sub-modules: ``fp8bs`` (the binding, loaded on first use of a public name),
 
 _PUBLIC = (
     "quantize_1x128", "quantize_transpose_128x1", "quantize_128x128", "quantize_dual",
-    "transpose_128x128", "gemm", "gemm_splitk", "splitk_workspace_bytes", "gemm_fused_quantize", "gemm_wgrad",
-    "grouped_gemm_contiguous", "grouped_gemm_masked",
+    "transpose_128x128", "gemm", "gemm_splitk", "gemm_splitk_noalloc", "splitk_workspace_bytes",
+    "gemm_fused_quantize", "gemm_wgrad", "grouped_gemm_contiguous", "grouped_gemm_masked",
     "cast_to_e4m3", "gemm_tile", "stream_reference", "abi_version", "Fp8bsError", "library",
 )
 

@@ -3,6 +3,7 @@
 // include/fp8bs.h next to each declaration.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -39,6 +40,29 @@ fp8bs_status launched(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_
 
 constexpr int64_t kMaxGridY = 65535;
 constexpr int64_t kMaxGridX = 0x7FFFFFFF;
+
+// Scratch of the allocation-free split-K call: the largest split-K
+// workspace (at most 256 partial tiles of 128 x 96 FP32), one copy per GPU,
+// held until the process ends.  Host code uses the device address that
+// hipGetSymbolAddress returns for the current device, never the symbol.
+constexpr int64_t kScratchBytes = 256 * 128 * 96 * 4;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call on that
+// device); nullptr if the lookup fails.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -201,6 +225,25 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled_splitk(const uint8_t* a, const float* sa
                 (flags & FP8BS_SCALE_POW2) != 0, fp8bs::kDense};
   (void)hipGetLastError();
   return launched(fp8bs::launch_gemm_splitk(p, static_cast<float*>(workspace), (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_gemm_fp8_blockscaled_splitk_noalloc(const uint8_t* a, const float* sa, const uint8_t* b,
+                                                       const float* sb, void* d, int64_t M, int64_t N, int64_t K,
+                                                       int32_t out_dtype, uint32_t flags, fp8bs_stream_t stream) {
+  if (M < 0) return FP8BS_ERR_SHAPE;
+  if (fp8bs_status e = gemm_common(N, K, out_dtype)) return e;
+  if (!grid_fits(M, N, 1) || !buffers_fit(M, N, K, false)) return FP8BS_ERR_SHAPE;
+  if (fp8bs::splitk_workspace_bytes(M, N, K) > kScratchBytes) return FP8BS_ERR_SHAPE;
+  if (flags & ~(uint32_t)FP8BS_SCALE_POW2) return FP8BS_ERR_FLAGS;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (fp8bs_status e = gemm_pointers(a, sa, b, sb, d, nullptr, false)) return e;
+  if (fp8bs_status e = check_device()) return e;
+  void* ws = scratch_ptr();
+  if (!ws) return FP8BS_ERR_DEVICE;
+  GemmProblem p{a, sa, b, sb, d, nullptr, M, N, K, 1, out_dtype == FP8BS_OUT_FP32, false,
+                (flags & FP8BS_SCALE_POW2) != 0, fp8bs::kDense};
+  (void)hipGetLastError();
+  return launched(fp8bs::launch_gemm_splitk(p, static_cast<float*>(ws), (hipStream_t)stream));
 }
 
 fp8bs_status fp8bs_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes) {

@@ -56,6 +56,7 @@ _gfq = _sig("fp8bs_gemm_fused_quantize", [_P, _P, _P, _P, _I64, _I64, _I64, _I32
 _gsplit = _sig("fp8bs_gemm_fp8_blockscaled_splitk",
                [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _U32, _P, _I64, _P])
 _gsplit_ws = _sig("fp8bs_gemm_splitk_workspace", [_I64, _I64, _I64, _P])
+_gsplit_na = _sig("fp8bs_gemm_fp8_blockscaled_splitk_noalloc", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _U32, _P])
 _lib.fp8bs_status_str.argtypes = [ctypes.c_int]
 _lib.fp8bs_status_str.restype = ctypes.c_char_p
 _lib.fp8bs_abi_version.argtypes = []
@@ -273,6 +274,22 @@ def gemm_splitk(a, sa, b, sb, out_dtype=torch.bfloat16, out=None, pow2_scales=Fa
     _check(_gsplit(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, code,
                    SCALE_POW2 if pow2_scales else 0, _ptr(workspace), workspace.numel(), _stream(a)),
            "gemm_fp8_blockscaled_splitk")
+    return out
+
+
+def gemm_splitk_noalloc(a, sa, b, sb, out):
+    """gemm_splitk into the caller's `out` (its dtype picks BF16 or FP32)
+    with the library's fixed per-GPU scratch instead of a workspace: no
+    device memory is allocated.  Calls on one GPU must not overlap in time."""
+    _codes(a, "a"); _codes(b, "b")
+    _need(sa, "sa", torch.float32, 2)
+    _need(sb, "sb", torch.float32, 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("operand or output shapes do not match")
+    _check(_gsplit_na(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, _out_code(out.dtype), 0,
+                      _stream(a)), "gemm_fp8_blockscaled_splitk_noalloc")
     return out
 
 

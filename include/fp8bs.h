@@ -48,7 +48,8 @@
  *   - The caller allocates, owns and frees every buffer; the library keeps no
  *     pointer after returning and allocates nothing.  The one call that needs
  *     scratch memory (fp8bs_gemm_fp8_blockscaled_splitk) takes it from the
- *     caller as a workspace argument.
+ *     caller as a workspace argument; its _noalloc variant uses a fixed
+ *     array the library holds on each GPU instead.
  *   - Every call enqueues its kernels on `stream` (NULL = the null stream) and
  *     returns without waiting; buffers must stay alive until the stream work
  *     completes.  Calls are re-entrant and thread-safe.
@@ -71,7 +72,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 8
+#define FP8BS_ABI_VERSION 9
 
 /* Same type as hipStream_t; declared here so the header needs no HIP headers. */
 struct ihipStream_t;
@@ -236,6 +237,27 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled_splitk(const uint8_t* a, const float* sa
                                                int32_t out_dtype, uint32_t flags,
                                                void* workspace, int64_t workspace_bytes,
                                                fp8bs_stream_t stream);
+
+/*
+ * fp8bs_gemm_fp8_blockscaled_splitk without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The partials go to a
+ * scratch array the library holds in each GPU's memory: 12 MiB (12582912
+ * bytes, 256 partial tiles), which covers every problem this call splits;
+ * a problem whose split would need more returns FP8BS_ERR_SHAPE (none does
+ * under the current split rule).  Nothing is allocated at call time; the
+ * array's device address is looked up on the first call on each device.
+ * Every call on one GPU shares that GPU's array, so calls that overlap in
+ * time on one GPU (other streams, other threads) race and may return wrong
+ * results: serialize them.  The array needs no clearing: each call writes
+ * every byte it reads.  Arguments and results as
+ * fp8bs_gemm_fp8_blockscaled_splitk.
+ */
+fp8bs_status fp8bs_gemm_fp8_blockscaled_splitk_noalloc(const uint8_t* a, const float* sa,
+                                                       const uint8_t* b, const float* sb,
+                                                       void* d, int64_t M, int64_t N, int64_t K,
+                                                       int32_t out_dtype, uint32_t flags,
+                                                       fp8bs_stream_t stream);
 
 /*
  * Workspace bytes fp8bs_gemm_fp8_blockscaled_splitk needs for M x N x K

@@ -46,7 +46,7 @@ def lib(lib_path):
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in fp8bs.h but not exported"
 
@@ -169,6 +169,33 @@ def test_splitk_validation(lib):
         assert f(*args, 4096, 2112, 7168, 0, 1, None, 0, None) == DEVICE     # no split: no workspace
 
 
+def test_splitk_noalloc_validation(lib):
+    f = fn(lib, "fp8bs_gemm_fp8_blockscaled_splitk_noalloc", [P, P, P, P, P, I64, I64, I64, I32, U32, P])
+    args = [FAKE] * 5
+    assert f(*args, 64, 100, 7168, 0, 0, None) == SHAPE            # N % 16
+    assert f(*args, 64, 2112, 7168, 2, 0, None) == FLAGS           # unknown out dtype
+    assert f(*args, 64, 2112, 7168, 0, 2, None) == FLAGS           # unknown flag bit
+    assert f(None, None, None, None, None, 0, 2112, 7168, 0, 0, None) == OK
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 64, 2112, 7168, 0, 0, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, MIS, 64, 2112, 7168, 0, 0, None) == ALIGN
+    if NO_DEVICE:
+        assert f(*args, 64, 2112, 7168, 0, 0, None) == DEVICE
+
+
+def test_splitk_workspace_never_exceeds_the_static_scratch(lib):
+    # the allocation-free variant's fixed array (12 MiB) covers every split:
+    # splits * tiles <= 256 partial tiles of 128 x 96 FP32
+    q = fn(lib, "fp8bs_gemm_splitk_workspace", [I64, I64, I64, P])
+    out = ctypes.c_int64(-1)
+    worst = 0
+    for M in (1, 64, 128, 129, 256, 384, 1000):
+        for N in (16, 96, 112, 208, 2112, 4096, 7168, 12288):
+            for K in (4096, 4224, 7168, 16384, 65536):
+                assert q(M, N, K, ctypes.byref(out)) == OK
+                worst = max(worst, out.value)
+    assert 0 < worst <= 256 * 128 * 96 * 4
+
+
 def test_grouped_validation(lib):
     fc = fn(lib, "fp8bs_grouped_gemm_fp8_contiguous", [P, P, P, P, P, P, I32, I64, I64, I64, I32, U32, P])
     fm = fn(lib, "fp8bs_grouped_gemm_fp8_masked", [P, P, P, P, P, P, I32, I64, I64, I64, I32, U32, P])
@@ -206,7 +233,7 @@ def test_cast_validation(lib):
 def test_binding_imports_and_reports_its_library(lib_path):
     from fp8_block_scaled_04_amd import fp8bs
     assert fp8bs.library() == lib_path
-    assert fp8bs.abi_version() == 8
+    assert fp8bs.abi_version() == 9
 
 
 def test_package_exports_every_binding_function(lib_path):
