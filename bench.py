@@ -210,6 +210,31 @@ def extra_kernels(fb, synth):
     del bsets, wb
     torch.cuda.empty_cache()
 
+    # The pages' Table 1 shapes (DeepGEMM on Hopper; their times are context,
+    # not targets): the few-row ones on the split-K GEMM, beside the unsplit
+    # GEMM on the same operands; weights rotated over >= 512 MB.
+    for (M, N, K, pages_us) in ((64, 2112, 7168, 9.41), (128, 7168, 2048, 7.37), (4096, 4096, 7168, 184.45)):
+        w = synth.dense(M, N, K, seed=0)
+        a, sa = fb.quantize_1x128(dev_bf16(w["a"]))
+        wb = dev_bf16(w["b"])
+        R = rotation(N * K)
+        bsets = [fb.quantize_128x128(wb) for _ in range(R)]
+        del wb
+        d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(16, fb.splitk_workspace_bytes(M, N, K)), dtype=torch.uint8, device="cuda")
+        it = iter(range(10 ** 9))
+        us_u, how = time_graph(lambda: fb.gemm(a, sa, *bsets[next(it) % R], out=d))
+        us, how = time_graph(lambda: fb.gemm_splitk(a, sa, *bsets[next(it) % R], out=d, workspace=ws))
+        tiles = ((M + 127) // 128) * ((N + 95) // 96)
+        byt = M * K + N * K + 2 * M * N + 4 * (K // 128) * (M + (N + 127) // 128)
+        out[f"gemm_pages_table1_{M}x{N}x{K}"] = dict(
+            us=us, timing=how, TFLOPs=2 * M * N * K / us / 1e6, GBs=byt / us / 1e3,
+            frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, frac_mfma=2 * M * N * K / us / 1e6 / FP8_PEAK_TFLOPS,
+            splits=fb.splitk_workspace_bytes(M, N, K) // (tiles * 128 * 96 * 4) or 1, us_unsplit=us_u,
+            pages_hopper_us=pages_us)
+        del bsets, ws, a, sa, d
+        torch.cuda.empty_cache()
+
     # MoE contiguous 8 x (sum M = 8192) x 4096 x 7168
     G, Mt, N, K = 8, 8192, 4096, 7168
     w = synth.contiguous(G, Mt, N, K, seed=0)

@@ -929,9 +929,16 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   const int64_t tile = (c / BN) * tiles_m + m / BM;
   const float* pp = ws + tile * S * (BM * BN) + (m % BM) * BN + c % BN;
   float4 v = *reinterpret_cast<const float4*>(pp);
-  for (int s = 1; s < S; ++s) {
-    const float4 w = *reinterpret_cast<const float4*>(pp + (int64_t)s * (BM * BN));
-    v = make_float4(v.x + w.x, v.y + w.y, v.z + w.z, v.w + w.w);
+  // eight partials loaded at a time (all in flight), then added in order
+  constexpr int U = 8;
+  for (int s = 1; s < S; s += U) {
+    float4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s + u < S) w[u] = *reinterpret_cast<const float4*>(pp + (int64_t)(s + u) * (BM * BN));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s + u < S) v = make_float4(v.x + w[u].x, v.y + w[u].y, v.z + w[u].z, v.w + w[u].w);
   }
   if (OUT_F32) *reinterpret_cast<float4*>(reinterpret_cast<float*>(d) + m * N + c) = v;
   else *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(d) + m * N + c) = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
