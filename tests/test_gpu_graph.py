@@ -146,3 +146,42 @@ def test_graph_replays_fused_quantize_gemm():
         assert np.array_equal(d.view(torch.int16).cpu().numpy(), want), f"replay {rep}"
         fp8bs.gemm_fused_quantize(x, b, sb)      # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_graph_replays_splitk_gemm():
+    """The split-K GEMM (partials kernel + reduction kernel, caller workspace)
+    and its allocation-free variant captured in one graph: every replay, with
+    eager calls of both between replays, equals the eager results."""
+    M, N, K = 64, 2112, 7168
+    print(f"graph capture split-K gemm M={M} N={N} K={K}", flush=True)
+    w = synth.dense(M, N, K, seed=9)
+    a, sa = fp8bs.quantize_1x128(bf16_dev(w["a"]))
+    b, sb = fp8bs.quantize_128x128(bf16_dev(w["b"]))
+    ws = torch.empty(fp8bs.splitk_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    d1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    d2 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+    def step():
+        fp8bs.gemm_splitk(a, sa, b, sb, out=d1, workspace=ws)
+        fp8bs.gemm_splitk_noalloc(a, sa, b, sb, d2)
+
+    step()
+    torch.cuda.synchronize()
+    want1, want2 = d1.view(torch.int16).cpu().numpy().copy(), d2.view(torch.int32).cpu().numpy().copy()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        d1.zero_(); d2.zero_(); ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(d1.view(torch.int16).cpu().numpy(), want1), f"replay {rep}: split-K (workspace)"
+        assert np.array_equal(d2.view(torch.int32).cpu().numpy(), want2), f"replay {rep}: split-K (no allocation)"
+        step()
+        torch.cuda.synchronize()
