@@ -110,6 +110,17 @@ using Tile192 = Cfg<192, 192, 3, 4, false, 3, true>;
 // Memory-bound shapes (few rows): 128x96 tiles, three stages, one
 // workgroup per CU on the 24576-column decode projection.
 using StreamTile = Cfg<128, 96, 2, 2, false, 3>;
+// Few rows and too few 128x96 tiles to fill the GPU: 64x64 tiles (two waves
+// of 64x32), four stages, two workgroups per CU.  Each CU then takes a
+// smaller share of the operands: 128 instead of 224 bytes per K column of
+// its tile.  Interleaved A/B against 128x96 on rotating weight sets,
+// outputs bit-identical: 128x7168x2048 13.8 -> 10.1 us, 128x8192x2048 14.2
+// -> 9.9 us, 96x4096x7168 34.4 -> 20.4 us, 64x2112x7168 28.1 -> 20.9 us,
+// 128x12288x1536 (384 tiles) 13.0 -> 12.4 us.  Three stages were slower on
+// every shape (up to 25 %), and five, six or eight no faster.  At 768 tiles
+// (128x24576x1536) it takes 16.0 against 13.9 us, so the decode projection
+// keeps 128x96.
+using Stream64Tile = Cfg<64, 64, 1, 2, false, 4>;
 // Masked (decode-time MoE) layout: 128x256 tiles with three stages (64 KB
 // of weights in flight per CU; an expert above 128 rows takes two row tiles,
 // which run next to each other and share the weight panel in L2).  Waves
@@ -409,6 +420,7 @@ __global__ __launch_bounds__(C::THREADS) void k_gemm(const GemmArgs p) {
     // slot when i % 4 would be slot 0 or 1, which the next chunk's first two
     // fragments are read into during the last row.
     static_assert(C::FM == 4, "the last row is written for four activation fragments");
+    static_assert(C::FN >= 2, "rows() computes at least one row before the last");
     constexpr int FN = C::FN;
     constexpr bool EXTRA = (FN % 4 == 1) || (FN % 4 == 2);
     constexpr int SLOTS = EXTRA ? 5 : 4;
@@ -824,7 +836,7 @@ double est_rounds(int64_t tiles, double cost) {
 }
 
 // Tile configurations the dispatcher chooses from.
-enum TileChoice { kStream, kSmall, kLarge, kMid, kT192, kPP192, kMaskedT, kWgradMid };
+enum TileChoice { kStream, kStream64, kSmall, kLarge, kMid, kT192, kPP192, kMaskedT, kWgradMid };
 
 template <int MODE>
 TileChoice choose(const GemmProblem& p) {
@@ -836,9 +848,10 @@ TileChoice choose(const GemmProblem& p) {
     return masked_tiles >= 256 ? kMaskedT : kSmall;
   } else {
     // Few rows (decode): the weights stream from HBM once; a deep pipeline
-    // over many small tiles keeps enough bytes in flight.
+    // over many small tiles keeps enough bytes in flight.  64x64 tiles up to
+    // one and a half per CU, else 128x96.
     if constexpr (MODE == kDense) {
-      if (p.M <= 128) return kStream;
+      if (p.M <= 128) return ((p.M + 63) / 64) * ((p.N + 63) / 64) <= 384 ? kStream64 : kStream;
     }
     // Row tiles: dense exact; contiguous counts on average half a partial
     // tile per group.
@@ -871,7 +884,7 @@ TileChoice choose(const GemmProblem& p) {
 // instantiated.
 constexpr bool possible(int mode, TileChoice c) {
   switch (mode) {
-    case kDense: return c == kStream || c == kSmall || c == kLarge || c == kMid || c == kT192 || c == kPP192;
+    case kDense: return c == kStream || c == kStream64 || c == kSmall || c == kLarge || c == kMid || c == kT192 || c == kPP192;
     case kContiguous: return c == kSmall || c == kLarge || c == kMid || c == kPP192;
     case kMasked: return c == kMaskedT || c == kSmall;
     default: return c == kLarge || c == kWgradMid;
@@ -888,6 +901,7 @@ template <int MODE>
 hipError_t dispatch(const GemmProblem& p, hipStream_t stream) {
   switch (choose<MODE>(p)) {
     case kStream: return launch_if<StreamTile, MODE, kStream>(p, stream);
+    case kStream64: return launch_if<Stream64Tile, MODE, kStream64>(p, stream);
     case kSmall: return launch_if<SmallTile, MODE, kSmall>(p, stream);
     case kLarge: return launch_if<LargeTile, MODE, kLarge>(p, stream);
     case kT192: return launch_if<Tile192, MODE, kT192>(p, stream);
@@ -903,6 +917,7 @@ void tile_of(const GemmProblem& p, int32_t& bm, int32_t& bn, int32_t& pp) {
   pp = 0;
   switch (choose<MODE>(p)) {
     case kStream: bm = StreamTile::BM; bn = StreamTile::BN; break;
+    case kStream64: bm = Stream64Tile::BM; bn = Stream64Tile::BN; break;
     case kSmall: bm = SmallTile::BM; bn = SmallTile::BN; break;
     case kLarge: bm = LargeTile::BM; bn = LargeTile::BN; break;
     case kT192: bm = Tile192::BM; bn = Tile192::BN; break;

@@ -344,7 +344,7 @@ def test_gemm_tile_query_validation(lib):
     assert f(3, 128, 256, 512, 1, 2, o, o + 4, o + 8) == FLAGS          # unknown flag
     assert f(3, 128, 256, 512, 1, 1, o, o + 4, o + 8) == OK             # power-of-two weight gradient
     assert f(0, 128, 256, 512, 1, 0, None, o + 4, o + 8) == NULL
-    assert f(0, 128, 256, 512, 1, 0, o, o + 4, o + 8) == OK and tuple(out) == (128, 96, 0)
+    assert f(0, 128, 256, 512, 1, 0, o, o + 4, o + 8) == OK and tuple(out) == (64, 64, 0)
 
 
 # The tile each benchmark workload and each labelled parity case runs on
@@ -355,6 +355,11 @@ TILES = [
     (("dense", 4001, 2112, 7168), (192, 192, 0)),        # rows not a multiple of 4: the other loop
     (("dense", 8192, 4096, 7168), (256, 256, 0)),
     (("dense", 128, 24576, 1536), (128, 96, 0)),         # decode
+    (("dense", 128, 7168, 2048), (64, 64, 0)),           # few rows, too few 128x96 tiles
+    (("dense", 128, 12288, 1536), (64, 64, 0)),          # 384 tiles of 64x64: the most it takes
+    (("dense", 128, 12352, 1536), (128, 96, 0)),         # 386
+    (("dense", 100, 13328, 384), (128, 96, 0)),          # ragged rows and columns on 128x96
+    (("dense", 37, 208, 1152), (64, 64, 0)),
     (("dense", 4096, 7168, 2176), (256, 256, 0)),        # data gradient
     (("dense", 4000, 7168, 256), (256, 256, 0)),         # ragged rows on 256x256
     (("dense", 4096, 4096, 256), (256, 256, 0)),

@@ -41,7 +41,10 @@ def run(a, sa, b, sb, out_dtype=torch.bfloat16):
                                    # then ragged rows (4000 = 15.6 tiles) on it
                                    (4096, 4096, 256), (4000, 7168, 256),
                                    # the 192x192 tile (ragged edges), then the 256x160 tile
-                                   (4000, 4112, 384), (2304, 4096, 256), (2560, 3584, 384)])
+                                   (4000, 4112, 384), (2304, 4096, 256), (2560, 3584, 384),
+                                   # few rows: the 64x64 tile (two row tiles, the second ragged;
+                                   # ragged columns), then 128x96 (ragged rows and columns)
+                                   (100, 208, 1152), (100, 13328, 384)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_gemm_workload_recipe(M, N, K, out_dtype):
     print(f"gemm M={M} N={N} K={K} out={out_dtype}", flush=True)
@@ -57,7 +60,9 @@ def test_gemm_workload_recipe(M, N, K, out_dtype):
 @pytest.mark.parametrize("M,N,K", [(256, 272, 1024),
                                    # 192x192 and 256x160 tiles: a wave's columns straddle two
                                    # weight blocks
-                                   (4000, 4112, 256), (2560, 3584, 256)])
+                                   (4000, 4112, 256), (2560, 3584, 256),
+                                   # the 64x64 and 128x96 tiles of few-row shapes
+                                   (100, 208, 640), (100, 13328, 256)])
 def test_gemm_exact_integer_inputs_bit_exact(M, N, K, out_dtype):
     # codes with integer values in [-16, 16] and power-of-two scales: every
     # partial sum is exact in FP32, so the output is the one rounding of the
@@ -138,3 +143,32 @@ def test_gemm_192_tile_chunk_counts(M, N, K):
     d = run(a, sa, b, sb, torch.float32)
     assert_gemm_close(out_host_f64(d), gemm.round_out(ref, "f32").astype(np.float64), f"gemm {M}x{N}x{K} f32",
                       dense_allowance(a, sa, b, sb))
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 512, 640, 1152])
+def test_gemm_64_tile_chunk_counts(K):
+    # the 64x64 tile's four-stage pipeline with 1, 2, 3, 4, 5 and 9 chunks
+    # (loop and tail); ragged last row and column tiles; BF16 and FP32 out
+    M, N = 100, 208
+    print(f"gemm 64 tile M={M} N={N} K={K}", flush=True)
+    assert fp8bs.gemm_tile("dense", M, N, K) == (64, 64, 0)
+    a, sa, b, sb = operands(M, N, K, seed=3 * K + 1)
+    ref = gemm.gemm_f64(a, sa, b, sb)
+    d = run(a, sa, b, sb)
+    assert_gemm_close(out_host_f64(d), bf16.to_f32(gemm.round_out(ref, "bf16")).astype(np.float64), f"gemm {M}x{N}x{K}",
+                      dense_allowance(a, sa, b, sb))
+    d = run(a, sa, b, sb, torch.float32)
+    assert_gemm_close(out_host_f64(d), gemm.round_out(ref, "f32").astype(np.float64), f"gemm {M}x{N}x{K} f32",
+                      dense_allowance(a, sa, b, sb))
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 7168, 2048), (64, 2112, 7168)])
+def test_gemm_few_rows_full_size(M, N, K):
+    # the pages' Table 1 shapes with few tokens, unsplit, on the 64x64 tile:
+    # every output against the float64 definition, rms over all of them
+    print(f"gemm full size {M}x{N}x{K}", flush=True)
+    assert fp8bs.gemm_tile("dense", M, N, K) == (64, 64, 0)
+    a, sa, b, sb = operands(M, N, K, seed=M + N)
+    d = run(a, sa, b, sb)
+    ref = bf16.to_f32(gemm.gemm_ref(a, sa, b, sb)).astype(np.float64)
+    assert_gemm_close(out_host_f64(d), ref, f"gemm {M}x{N}x{K}", dense_allowance(a, sa, b, sb))
