@@ -42,7 +42,7 @@ constexpr int64_t kMaxGridY = 65535;
 constexpr int64_t kMaxGridX = 0x7FFFFFFF;
 
 // Scratch of the allocation-free split-K call: the largest split-K
-// workspace (at most 256 partial tiles of 128 x 96 FP32), one copy per GPU,
+// workspace (at most 256 partial tiles of at most 128 x 96 FP32), one copy per GPU,
 // held until the process ends.  Host code uses the device address that
 // hipGetSymbolAddress returns for the current device, never the symbol.
 constexpr int64_t kScratchBytes = 256 * 128 * 96 * 4;

@@ -931,12 +931,21 @@ void tile_of(const GemmProblem& p, int32_t& bm, int32_t& bn, int32_t& pp) {
 // ---- split K --------------------------------------------------------------
 // D[m][n] = sum over the splits s = 0, 1, .. of partial s of the tile holding
 // (m, n), added in that order (four outputs of one row per lane).
-using SplitTile = StreamTile;
+// Split tiles: 64x64 for at most 128 rows, 128x96 above (interleaved A/B on
+// rotating weight sets, graph-timed: 64x2112x7168 12.9 -> 10.9 us,
+// 128x2112x7168 16.7 -> 13.6 us, 32x4096x7168 13.1 -> 12.1 us; but
+// 256x2112x7168 18.0 -> 20.2 us).
+template <class T>
+int64_t split_tiles(int64_t M, int64_t N) {
+  return ((M + T::BM - 1) / T::BM) * ((N + T::BN - 1) / T::BN);
+}
+bool split_on_64(int64_t M) { return M <= 128; }
 
-template <bool OUT_F32>
+template <class T, bool OUT_F32>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, void* __restrict__ d, int64_t M,
                                                        int64_t N, int32_t S, int32_t tiles_m) {
-  constexpr int BM = SplitTile::BM, BN = SplitTile::BN;
+  constexpr int BM = T::BM, BN = T::BN;
+  static_assert(BN % 4 == 0, "a lane's four outputs lie in one tile");
   const int64_t n4 = N / 4;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= M * n4) return;
@@ -959,16 +968,38 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   else *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(d) + m * N + c) = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
 }
 
+template <class T>
+hipError_t launch_split(const GemmProblem& pr, float* ws, int32_t S, hipStream_t stream) {
+  GemmArgs a;
+  a.a = pr.a; a.sa = pr.sa; a.b = pr.b; a.sb = pr.sb; a.d = ws; a.groups = nullptr;
+  a.M = pr.M; a.N = pr.N; a.K = pr.K; a.G = S;
+  a.tiles_m = (int32_t)((pr.M + T::BM - 1) / T::BM);
+  a.tiles_n = (int32_t)((pr.N + T::BN - 1) / T::BN);
+  a.group_m = 8;
+  a.accumulate = 0;
+  const dim3 grid((unsigned)((int64_t)a.tiles_m * a.tiles_n * S)), block(T::THREADS);
+  if (pr.hw_scale) hipLaunchKernelGGL((k_gemm<T, kSplitK, true, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((k_gemm<T, kSplitK, true, false>), grid, block, 0, stream, a);
+  if (hipError_t e = hipGetLastError()) return e;
+  const int64_t outs = pr.M * (pr.N / 4);
+  const dim3 rgrid((unsigned)((outs + 255) / 256)), rblock(256);
+  if (pr.out_f32)
+    hipLaunchKernelGGL((k_splitk_reduce<T, true>), rgrid, rblock, 0, stream, ws, pr.d, pr.M, pr.N, S, a.tiles_m);
+  else
+    hipLaunchKernelGGL((k_splitk_reduce<T, false>), rgrid, rblock, 0, stream, ws, pr.d, pr.M, pr.N, S, a.tiles_m);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-// Splits: as many as fill one round of the 256 CUs with the 128x96 tiles
-// (one workgroup per CU), with at least two chunks each and at most 32; only
-// for K of at least 32 chunks, where the split saves more than the second
-// launch and the partials' round trip cost (measured: 64 x 2112 x 7168 28.4
-// -> 15.6 us with 11 splits, 256 x 2112 x 7168 50.4 -> 17.7 us with 5, but
-// 128 x 7168 x 2048, 16 chunks, 13.8 -> 16.8 us with 3).
+// Splits: as many as fill one round of the 256 CUs with the split tiles (one
+// workgroup per CU), with at least two chunks each and at most 32; only for
+// K of at least 32 chunks, where the split saves more than the second launch
+// and the partials' round trip cost (measured on 128x96 split tiles: 64 x
+// 2112 x 7168 28.4 -> 15.6 us with 11 splits, 256 x 2112 x 7168 50.4 -> 17.7
+// us with 5, but 128 x 7168 x 2048, 16 chunks, 13.8 -> 16.8 us with 3).
 int32_t splitk_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + SplitTile::BM - 1) / SplitTile::BM) * ((N + SplitTile::BN - 1) / SplitTile::BN);
+  const int64_t tiles = split_on_64(M) ? split_tiles<Stream64Tile>(M, N) : split_tiles<StreamTile>(M, N);
   const int64_t kt = K / kKC;
   if (tiles <= 0 || kt < 32) return 1;
   int64_t s = 256 / tiles;
@@ -980,31 +1011,16 @@ int32_t splitk_splits(int64_t M, int64_t N, int64_t K) {
 int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const int32_t s = splitk_splits(M, N, K);
   if (s < 2) return 0;
-  const int64_t tiles = ((M + SplitTile::BM - 1) / SplitTile::BM) * ((N + SplitTile::BN - 1) / SplitTile::BN);
-  return tiles * s * SplitTile::BM * SplitTile::BN * (int64_t)sizeof(float);
+  const int64_t tile_bytes = (split_on_64(M) ? Stream64Tile::BM * Stream64Tile::BN : StreamTile::BM * StreamTile::BN) *
+                             (int64_t)sizeof(float);
+  const int64_t tiles = split_on_64(M) ? split_tiles<Stream64Tile>(M, N) : split_tiles<StreamTile>(M, N);
+  return tiles * s * tile_bytes;
 }
 
 hipError_t launch_gemm_splitk(const GemmProblem& pr, float* ws, hipStream_t stream) {
   const int32_t S = splitk_splits(pr.M, pr.N, pr.K);
   if (S < 2) return launch_gemm(pr, stream);
-  GemmArgs a;
-  a.a = pr.a; a.sa = pr.sa; a.b = pr.b; a.sb = pr.sb; a.d = ws; a.groups = nullptr;
-  a.M = pr.M; a.N = pr.N; a.K = pr.K; a.G = S;
-  a.tiles_m = (int32_t)((pr.M + SplitTile::BM - 1) / SplitTile::BM);
-  a.tiles_n = (int32_t)((pr.N + SplitTile::BN - 1) / SplitTile::BN);
-  a.group_m = 8;
-  a.accumulate = 0;
-  const dim3 grid((unsigned)((int64_t)a.tiles_m * a.tiles_n * S)), block(SplitTile::THREADS);
-  if (pr.hw_scale) hipLaunchKernelGGL((k_gemm<SplitTile, kSplitK, true, true>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((k_gemm<SplitTile, kSplitK, true, false>), grid, block, 0, stream, a);
-  if (hipError_t e = hipGetLastError()) return e;
-  const int64_t outs = pr.M * (pr.N / 4);
-  const dim3 rgrid((unsigned)((outs + 255) / 256)), rblock(256);
-  if (pr.out_f32)
-    hipLaunchKernelGGL(k_splitk_reduce<true>, rgrid, rblock, 0, stream, ws, pr.d, pr.M, pr.N, S, a.tiles_m);
-  else
-    hipLaunchKernelGGL(k_splitk_reduce<false>, rgrid, rblock, 0, stream, ws, pr.d, pr.M, pr.N, S, a.tiles_m);
-  return hipGetLastError();
+  return split_on_64(pr.M) ? launch_split<Stream64Tile>(pr, ws, S, stream) : launch_split<StreamTile>(pr, ws, S, stream);
 }
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {

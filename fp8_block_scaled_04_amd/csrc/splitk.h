@@ -1,6 +1,7 @@
 // Split-K dense GEMM (host side).  For shapes with too few output tiles to
 // fill the GPU (few rows and few columns: decode-sized activations), the K
-// chunks of each 128x96 output tile are split over several workgroups.
+// chunks of each output tile (64x64 for at most 128 rows, else 128x96) are
+// split over several workgroups.
 // Each writes its FP32 partial of the tile (its chunks, promoted per chunk
 // exactly as in the unsplit kernel) to a caller-provided workspace; a second
 // kernel adds the partials in split order and writes D.  The promotion is

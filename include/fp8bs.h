@@ -214,7 +214,8 @@ fp8bs_status fp8bs_gemm_fp8_blockscaled(const uint8_t* a, const float* sa,
  * Deepgemm", Table 1 "DeepGemm Performance Benchmarks": its row with M = 64,
  * N = 2112, K = 7168; page 2, paragraph on decoding, where few tokens make the
  * GEMM memory-bound).  It splits only where K has at least 32 chunks (with at
- * least two per split).  Each 128 x 96 output tile is computed by S workgroups, one
+ * least two per split).  Each output tile (64 x 64 for M <= 128, else 128 x 96)
+ * is computed by S workgroups, one
  * per range of K chunks, each promoting its chunks into FP32 exactly as the
  * unsplit GEMM does; the S FP32 partials are then added in split order and
  * rounded once to the output type.  The result equals the unsplit GEMM's up to

@@ -137,9 +137,12 @@ def test_gemm_validation(lib):
 def test_splitk_workspace_query(lib):
     q = fn(lib, "fp8bs_gemm_splitk_workspace", [I64, I64, I64, P])
     out = ctypes.c_int64(-1)
-    # the pages' decode-sized rows: 22 tiles of 128x96 -> 11 splits
-    assert q(64, 2112, 7168, ctypes.byref(out)) == OK and out.value == 22 * 11 * 128 * 96 * 4
-    # 44 tiles -> 5 splits
+    # the pages' decode-sized rows: 33 tiles of 64x64 -> 7 splits
+    assert q(64, 2112, 7168, ctypes.byref(out)) == OK and out.value == 33 * 7 * 64 * 64 * 4
+    # at most 128 rows on 64x64 split tiles, more on 128x96: 66 tiles -> 3
+    # splits; 44 tiles -> 5 splits
+    assert q(128, 2112, 7168, ctypes.byref(out)) == OK and out.value == 66 * 3 * 64 * 64 * 4
+    assert q(129, 2112, 7168, ctypes.byref(out)) == OK and out.value == 44 * 5 * 128 * 96 * 4
     assert q(256, 2112, 7168, ctypes.byref(out)) == OK and out.value == 44 * 5 * 128 * 96 * 4
     # enough tiles already, or fewer than 32 chunks: no split, no workspace
     assert q(4096, 2112, 7168, ctypes.byref(out)) == OK and out.value == 0
@@ -154,7 +157,7 @@ def test_splitk_workspace_query(lib):
 
 def test_splitk_validation(lib):
     f = fn(lib, "fp8bs_gemm_fp8_blockscaled_splitk", [P, P, P, P, P, I64, I64, I64, I32, U32, P, I64, P])
-    ws = 22 * 11 * 128 * 96 * 4
+    ws = 33 * 7 * 64 * 64 * 4
     args = [FAKE] * 5
     assert f(*args, 64, 100, 7168, 0, 0, FAKE, ws, None) == SHAPE            # N % 16
     assert f(*args, 64, 2112, 7168, 0, 0, FAKE, ws - 1, None) == SHAPE       # workspace too small
@@ -184,7 +187,7 @@ def test_splitk_noalloc_validation(lib):
 
 def test_splitk_workspace_never_exceeds_the_static_scratch(lib):
     # the allocation-free variant's fixed array (12 MiB) covers every split:
-    # splits * tiles <= 256 partial tiles of 128 x 96 FP32
+    # splits * tiles <= 256 partial tiles of at most 128 x 96 FP32
     q = fn(lib, "fp8bs_gemm_splitk_workspace", [I64, I64, I64, P])
     out = ctypes.c_int64(-1)
     worst = 0

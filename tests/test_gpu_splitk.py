@@ -7,7 +7,8 @@ ref = float64 definition rounded once to the output dtype; bit-exact (and
 bit-identical to the unsplit GEMM) when every partial sum is exact in FP32
 (exact-integer inputs).  Shapes include the pages' Table 1 rows with few
 tokens (M = 64, split; M = 128 with K = 2048, not split), ragged row and
-column tiles, uneven chunk counts per split, the split cap, and a single chunk.
+column tiles on both split tiles (64x64 up to 128 rows, 128x96 above), uneven
+chunk counts per split, the split cap, and a single chunk.
 """
 
 import numpy as np
@@ -21,7 +22,9 @@ from tests.gpu_util import (assert_codes_equal, assert_gemm_close, codes_dev, de
 
 pytestmark = pytest.mark.gpu
 
-TILE = 128 * 96 * 4   # workspace bytes per tile partial
+def tile_bytes(M):
+    # workspace bytes per tile partial: 64x64 split tiles up to 128 rows, else 128x96
+    return (64 * 64 if M <= 128 else 128 * 96) * 4
 
 
 def setup_module(module):
@@ -48,19 +51,21 @@ def ref_out(a, sa, b, sb, out_dtype):
             else gemm.round_out(r, "f32")).astype(np.float64)
 
 
-# (M, N, K, tiles of 128x96, splits)
-SHAPES = [(64, 2112, 7168, 22, 11),    # Table 1, M = 64
-          (256, 2112, 7168, 44, 5),    # two row tiles
-          (37, 208, 4608, 3, 18),      # ragged rows and columns, two chunks per split
+# (M, N, K, split tiles, splits)
+SHAPES = [(64, 2112, 7168, 33, 7),     # Table 1, M = 64 (64x64 split tiles)
+          (128, 2112, 7168, 66, 3),    # two 64-row tiles, 56 chunks over 3 splits
+          (100, 4112, 4224, 130, 1),   # too many tiles to split
+          (256, 2112, 7168, 44, 5),    # 128x96 split tiles, two row tiles
+          (37, 208, 4608, 4, 18),      # ragged rows and columns, two chunks per split
           (200, 400, 4224, 10, 16),    # 33 chunks over 16 splits: two or three each
           (130, 96, 8192, 2, 32),      # the split cap
-          (128, 7168, 2048, 75, 1),    # Table 1, M = 128: 16 chunks, not split
+          (128, 7168, 2048, 224, 1),   # Table 1, M = 128: 16 chunks, not split
           (1, 16, 128, 1, 1)]          # a single chunk: the unsplit GEMM
 
 
 @pytest.mark.parametrize("M,N,K,tiles,splits", SHAPES)
 def test_splitk_workspace_size(M, N, K, tiles, splits):
-    assert fp8bs.splitk_workspace_bytes(M, N, K) == (tiles * splits * TILE if splits > 1 else 0)
+    assert fp8bs.splitk_workspace_bytes(M, N, K) == (tiles * splits * tile_bytes(M) if splits > 1 else 0)
 
 
 @pytest.mark.parametrize("M,N,K,tiles,splits", SHAPES)
@@ -73,7 +78,7 @@ def test_splitk_workload_recipe(M, N, K, tiles, splits, out_dtype):
                       dense_allowance(a, sa, b, sb))
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (37, 208, 4608), (130, 96, 8192)])
+@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (37, 208, 4608), (128, 2112, 7168), (130, 96, 8192)])
 def test_splitk_pow2_scales(M, N, K):
     # power-of-two scales applied by the scaled MFMA inside each split
     print(f"split-K pow2 gemm M={M} N={N} K={K}", flush=True)
@@ -83,7 +88,7 @@ def test_splitk_pow2_scales(M, N, K):
                       dense_allowance(a, sa, b, sb))
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (200, 400, 4224), (130, 96, 8192)])
+@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (128, 2112, 7168), (200, 400, 4224), (130, 96, 8192)])
 @pytest.mark.parametrize("pow2", [False, True])
 def test_splitk_exact_integer_inputs_bit_exact(M, N, K, pow2):
     # integer codes in [-16, 16] and power-of-two scales: every partial and
