@@ -225,13 +225,15 @@ def extra_kernels(fb, synth):
         it = iter(range(10 ** 9))
         us_u, how = time_graph(lambda: fb.gemm(a, sa, *bsets[next(it) % R], out=d))
         us, how = time_graph(lambda: fb.gemm_splitk(a, sa, *bsets[next(it) % R], out=d, workspace=ws))
-        tiles = ((M + 127) // 128) * ((N + 95) // 96)
+        # split tiles: 64x64 up to 128 rows, else 128x96
+        tm, tn = (64, 64) if M <= 128 else (128, 96)
+        tiles = ((M + tm - 1) // tm) * ((N + tn - 1) // tn)
         byt = M * K + N * K + 2 * M * N + 4 * (K // 128) * (M + (N + 127) // 128)
         out[f"gemm_pages_table1_{M}x{N}x{K}"] = dict(
             us=us, timing=how, TFLOPs=2 * M * N * K / us / 1e6, GBs=byt / us / 1e3,
             frac_hbm=byt / us / 1e3 / HBM_PEAK_GBS, frac_mfma=2 * M * N * K / us / 1e6 / FP8_PEAK_TFLOPS,
-            splits=fb.splitk_workspace_bytes(M, N, K) // (tiles * 128 * 96 * 4) or 1, us_unsplit=us_u,
-            pages_hopper_us=pages_us)
+            splits=fb.splitk_workspace_bytes(M, N, K) // (tiles * tm * tn * 4) or 1, us_unsplit=us_u,
+            tile_unsplit=list(fb.gemm_tile("dense", M, N, K)[:2]), pages_hopper_us=pages_us)
         del bsets, ws, a, sa, d
         torch.cuda.empty_cache()
 
