@@ -110,7 +110,7 @@ using Tile192 = Cfg<192, 192, 3, 4, false, 3, true>;
 // Memory-bound shapes (few rows): 128x96 tiles, three stages, one
 // workgroup per CU on the 24576-column decode projection.
 using StreamTile = Cfg<128, 96, 2, 2, false, 3>;
-// Few rows and too few 128x96 tiles to fill the GPU: 64x64 tiles (two waves
+// Few rows and too few larger tiles to fill the GPU: 64x64 tiles (two waves
 // of 64x32), four stages, two workgroups per CU.  Each CU then takes a
 // smaller share of the operands: 128 instead of 224 bytes per K column of
 // its tile.  Interleaved A/B against 128x96 on rotating weight sets,
@@ -849,9 +849,16 @@ TileChoice choose(const GemmProblem& p) {
   } else {
     // Few rows (decode): the weights stream from HBM once; a deep pipeline
     // over many small tiles keeps enough bytes in flight.  64x64 tiles up to
-    // one and a half per CU, else 128x96.
+    // one and a half per CU, else 128x96.  Up to 512 rows the larger tiles
+    // leave most CUs idle while 64x64 tiles fill them: up to two per CU
+    // (interleaved A/B against the 128x128 tile the cost model picks,
+    // outputs bit-identical: 256x2112x7168 39.8 -> 20.4 us, 256x4096x7168
+    // 52.9 -> 22.9 us, 512x2112x7168 40.6 -> 24.2 us, 200x4096x4096 24.0 ->
+    // 14.6 us, 512x4096x2048 (512 tiles) 15.6 -> 13.3 us).
     if constexpr (MODE == kDense) {
-      if (p.M <= 128) return ((p.M + 63) / 64) * ((p.N + 63) / 64) <= 384 ? kStream64 : kStream;
+      const int64_t t64 = ((p.M + 63) / 64) * ((p.N + 63) / 64);
+      if (p.M <= 128) return t64 <= 384 ? kStream64 : kStream;
+      if (p.M <= 512 && t64 <= 512) return kStream64;
     }
     // Row tiles: dense exact; contiguous counts on average half a partial
     // tile per group.

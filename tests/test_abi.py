@@ -363,6 +363,10 @@ TILES = [
     (("dense", 128, 12352, 1536), (128, 96, 0)),         # 386
     (("dense", 100, 13328, 384), (128, 96, 0)),          # ragged rows and columns on 128x96
     (("dense", 37, 208, 1152), (64, 64, 0)),
+    (("dense", 256, 2112, 7168), (64, 64, 0)),           # up to 512 rows: 64x64 up to two per CU
+    (("dense", 512, 4096, 2048), (64, 64, 0)),           # 512 tiles of 64x64: the most it takes
+    (("dense", 512, 4112, 2048), (128, 128, 0)),         # 520
+    (("dense", 513, 144, 1152), (128, 128, 0)),          # past 512 rows
     (("dense", 4096, 7168, 2176), (256, 256, 0)),        # data gradient
     (("dense", 4000, 7168, 256), (256, 256, 0)),         # ragged rows on 256x256
     (("dense", 4096, 4096, 256), (256, 256, 0)),

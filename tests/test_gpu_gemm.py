@@ -44,7 +44,9 @@ def run(a, sa, b, sb, out_dtype=torch.bfloat16):
                                    (4000, 4112, 384), (2304, 4096, 256), (2560, 3584, 384),
                                    # few rows: the 64x64 tile (two row tiles, the second ragged;
                                    # ragged columns), then 128x96 (ragged rows and columns)
-                                   (100, 208, 1152), (100, 13328, 384)])
+                                   (100, 208, 1152), (100, 13328, 384),
+                                   # the 64x64 tile up to 512 rows, at its 512-tile limit
+                                   (384, 4096, 7168), (512, 4096, 2048)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_gemm_workload_recipe(M, N, K, out_dtype):
     print(f"gemm M={M} N={N} K={K} out={out_dtype}", flush=True)
@@ -61,8 +63,9 @@ def test_gemm_workload_recipe(M, N, K, out_dtype):
                                    # 192x192 and 256x160 tiles: a wave's columns straddle two
                                    # weight blocks
                                    (4000, 4112, 256), (2560, 3584, 256),
-                                   # the 64x64 and 128x96 tiles of few-row shapes
-                                   (100, 208, 640), (100, 13328, 256)])
+                                   # the 64x64 and 128x96 tiles of few-row shapes, then the
+                                   # 128x128 tile (past 512 rows) and 64x64 with ragged rows
+                                   (100, 208, 640), (100, 13328, 256), (513, 144, 1152), (300, 400, 640)])
 def test_gemm_exact_integer_inputs_bit_exact(M, N, K, out_dtype):
     # codes with integer values in [-16, 16] and power-of-two scales: every
     # partial sum is exact in FP32, so the output is the one rounding of the

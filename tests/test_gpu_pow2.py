@@ -47,7 +47,7 @@ def ref_out(a, sa, b, sb, out_dtype):
 # 4000x4112), 256x160 (2450x3696), 256x256, 64x64 and 128x96 (few rows), with ragged edges
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (37, 48, 384), (300, 400, 640), (4096, 2112, 1024), (4000, 7168, 256),
                                    (4096, 4096, 256), (4000, 4112, 384), (2450, 3696, 256), (128, 24576, 1536),
-                                   (1, 16, 128), (100, 208, 1152), (100, 13328, 384)])
+                                   (1, 16, 128), (100, 208, 1152), (100, 13328, 384), (513, 144, 1152)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_pow2_recipe(M, N, K, out_dtype):
     print(f"pow2 gemm M={M} N={N} K={K} out={out_dtype}", flush=True)
