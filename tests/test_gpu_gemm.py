@@ -175,3 +175,15 @@ def test_gemm_few_rows_full_size(M, N, K):
     d = run(a, sa, b, sb)
     ref = bf16.to_f32(gemm.gemm_ref(a, sa, b, sb)).astype(np.float64)
     assert_gemm_close(out_host_f64(d), ref, f"gemm {M}x{N}x{K}", dense_allowance(a, sa, b, sb))
+
+
+@pytest.mark.parametrize("M,N,K,pow2", [(4096, 4096, 7168, False), (128, 24576, 1536, False)])
+def test_gemm_pages_shapes_full_size(M, N, K, pow2):
+    # the pages' Table 1 shape with many tokens (256x256 tiles, one round)
+    # and the decode projection with FP32 scales: every output against the
+    # float64 definition, rms over all of them
+    print(f"gemm full size {M}x{N}x{K} pow2={pow2}", flush=True)
+    a, sa, b, sb = operands(M, N, K, seed=M + 2 * N, pow2=pow2)
+    d = run(a, sa, b, sb)
+    ref = bf16.to_f32(gemm.gemm_ref(a, sa, b, sb)).astype(np.float64)
+    assert_gemm_close(out_host_f64(d), ref, f"gemm {M}x{N}x{K}", dense_allowance(a, sa, b, sb))
