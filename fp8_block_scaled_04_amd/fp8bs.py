@@ -282,12 +282,17 @@ def gemm_splitk_noalloc(a, sa, b, sb, out):
     with the library's fixed per-GPU scratch instead of a workspace: no
     device memory is allocated.  Calls on one GPU must not overlap in time."""
     _codes(a, "a"); _codes(b, "b")
+    for t, n in ((a, "a"), (b, "b")):
+        _need(t, n, None, 2)
     _need(sa, "sa", torch.float32, 2)
     _need(sb, "sb", torch.float32, 2)
+    _need(out, "out", None, 2)
     M, K = a.shape
     N = b.shape[0]
     if b.shape[1] != K or tuple(out.shape) != (M, N):
         raise ValueError("operand or output shapes do not match")
+    if tuple(sa.shape) != (K // 128, M) or tuple(sb.shape) != ((N + 127) // 128, K // 128):
+        raise ValueError("scale shapes do not match the operands")
     _check(_gsplit_na(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), M, N, K, _out_code(out.dtype), 0,
                       _stream(a)), "gemm_fp8_blockscaled_splitk_noalloc")
     return out

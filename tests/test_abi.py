@@ -404,3 +404,20 @@ def test_stream_reference_validation(lib):
     assert f(MIS, 32, FAKE, 16, None) == ALIGN
     if NO_DEVICE:
         assert f(FAKE, 32, FAKE, 16, None) == DEVICE
+
+
+def test_binding_rejects_host_tensors_before_the_library(lib_path):
+    # host (or strided) tensors would hand the kernels pointers they cannot
+    # use: the binding refuses them before it calls the library
+    import torch
+    from fp8_block_scaled_04_amd import fp8bs
+    a = torch.zeros((64, 256), dtype=torch.uint8)
+    b = torch.zeros((128, 256), dtype=torch.uint8)
+    sa, sb = torch.ones((2, 64)), torch.ones((1, 2))
+    out = torch.empty((64, 128), dtype=torch.bfloat16)
+    calls = {"gemm": lambda: fp8bs.gemm(a, sa, b, sb, out=out),
+             "gemm_splitk": lambda: fp8bs.gemm_splitk(a, sa, b, sb, out=out),
+             "gemm_splitk_noalloc": lambda: fp8bs.gemm_splitk_noalloc(a, sa, b, sb, out)}
+    for name, call in calls.items():
+        with pytest.raises(ValueError, match="GPU tensor"):
+            call()
